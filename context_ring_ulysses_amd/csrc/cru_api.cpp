@@ -1,0 +1,471 @@
+// Host side of the C ABI declared in include/cru.h: argument checks, launch
+// set-up and the ring-share orchestration.  Nothing here computes attention;
+// every step of the path runs in the HIP kernels.
+//
+// The checks mirror the three classes of the diffusers "Attention backends"
+// page, "Checks" section (device, data type, shape) and the divisibility
+// rules of the diffusers "Context parallelism" guide's variant table (ring:
+// sequence length divisible by the ring degree unless "Ring Anything";
+// Ulysses: sequence length and head count divisible by the Ulysses degree).
+// They all run before anything is enqueued, so a failed call has no effect
+// on the device.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "cru.h"
+#include "cru_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+cru_status fail(cru_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+#define CRU_TRY(expr)                 \
+  do {                                \
+    cru_status st_ = (expr);          \
+    if (st_ != CRU_OK) return st_;    \
+  } while (0)
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+int elem_bytes(int dtype) { return dtype == CRU_BF16 ? 2 : 4; }
+const char* dtype_name(int dtype) { return dtype == CRU_BF16 ? "bf16" : "fp32"; }
+
+cru_status check_tensor(const cru_tensor* t, const char* name) {
+  if (t == nullptr) return fail(CRU_EINVAL, "%s: descriptor is NULL", name);
+  if (t->dtype != CRU_F32 && t->dtype != CRU_BF16)
+    return fail(CRU_EUNSUPPORTED, "%s: unknown dtype code %d", name, t->dtype);
+  if (t->reserved != 0) return fail(CRU_EINVAL, "%s: reserved field must be 0", name);
+  if (t->B < 0 || t->S < 0 || t->H < 0 || t->D < 0)
+    return fail(CRU_EINVAL, "%s: negative size", name);
+  if (t->B > kMaxDim || t->S > kMaxDim || t->H > kMaxDim || t->D > kMaxDim)
+    return fail(CRU_EINVAL, "%s: size above 2^30", name);
+  if (t->sb < 0 || t->ss < 0 || t->sh < 0) return fail(CRU_EINVAL, "%s: negative stride", name);
+  const int64_t numel = t->B * t->S * t->H * t->D;
+  if (numel > 0 && t->data == nullptr) return fail(CRU_EINVAL, "%s: data is NULL", name);
+  if (reinterpret_cast<uintptr_t>(t->data) % 16 != 0)
+    return fail(CRU_EINVAL, "%s: data is not 16-byte aligned", name);
+  const int64_t vec = 16 / elem_bytes(t->dtype);
+  if (t->sb % vec || t->ss % vec || t->sh % vec)
+    return fail(CRU_EINVAL, "%s: strides (%lld, %lld, %lld) are not multiples of %lld elements",
+                name, (long long)t->sb, (long long)t->ss, (long long)t->sh, (long long)vec);
+  return CRU_OK;
+}
+
+cru_status check_head_dim(const cru_tensor* t, const char* name) {
+  if (t->D != 64 && t->D != 128)
+    return fail(CRU_EUNSUPPORTED, "%s: head dim %lld (supported: 64, 128)", name, (long long)t->D);
+  return CRU_OK;
+}
+
+cru_status check_lse(const cru_lse* l, const char* name, int64_t B, int64_t H, int64_t S) {
+  if (l == nullptr) return fail(CRU_EINVAL, "%s: descriptor is NULL", name);
+  if (l->B != B || l->H != H || l->S != S)
+    return fail(CRU_EINVAL, "%s: shape [%lld, %lld, %lld], expected [%lld, %lld, %lld]", name,
+                (long long)l->B, (long long)l->H, (long long)l->S, (long long)B, (long long)H,
+                (long long)S);
+  if (l->sb < 0 || l->sh < 0) return fail(CRU_EINVAL, "%s: negative stride", name);
+  if (B * H * S > 0 && l->data == nullptr) return fail(CRU_EINVAL, "%s: data is NULL", name);
+  if (reinterpret_cast<uintptr_t>(l->data) % 4 != 0)
+    return fail(CRU_EINVAL, "%s: data is not 4-byte aligned", name);
+  return CRU_OK;
+}
+
+bool same_shape(const cru_tensor* a, const cru_tensor* b) {
+  return a->B == b->B && a->S == b->S && a->H == b->H && a->D == b->D;
+}
+
+cru_status check_device(const void* p, const char* name) {
+  if (p == nullptr) return CRU_OK;   // only empty tensors get here with NULL
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(CRU_EDEVICE, "%s: no current HIP device", name);
+  }
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(CRU_EDEVICE, "%s: pointer is not HIP device memory", name);
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+    return fail(CRU_EDEVICE, "%s: pointer is not device memory (memory type %d)", name,
+                (int)attr.type);
+  if (attr.device != dev)
+    return fail(CRU_EDEVICE, "%s: pointer is on device %d, current device is %d", name,
+                attr.device, dev);
+  return CRU_OK;
+}
+
+cru_status check_scale(float scale, int64_t D, float* scale_log2) {
+  if (!(scale >= 0.0f) || std::isinf(scale))
+    return fail(CRU_EINVAL, "scale must be finite and >= 0 (0 selects 1/sqrt(D)), got %g",
+                (double)scale);
+  const double sc = scale == 0.0f ? 1.0 / std::sqrt((double)D) : (double)scale;
+  *scale_log2 = (float)(sc * 1.4426950408889634);   // log2(e)
+  return CRU_OK;
+}
+
+cru_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(CRU_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return CRU_OK;
+}
+
+void fill_attn_views(cru::AttnArgs& a, const cru_tensor* q, const cru_tensor* k,
+                     const cru_tensor* v) {
+  a.q = q->data;
+  a.k = k->data;
+  a.v = v->data;
+  a.q_sb = q->sb; a.q_ss = q->ss; a.q_sh = q->sh;
+  a.k_sb = k->sb; a.k_ss = k->ss; a.k_sh = k->sh;
+  a.v_sb = v->sb; a.v_ss = v->ss; a.v_sh = v->sh;
+  a.B = (int)q->B;
+  a.H = (int)q->H;
+  a.Sq = (int)q->S;
+  a.D = (int)q->D;
+}
+
+// Checks shared by the attention entry points: q, k, v, o views, dtypes, shapes.
+cru_status check_qkvo(const cru_tensor* q, const cru_tensor* k, const cru_tensor* v,
+                      const cru_tensor* o) {
+  CRU_TRY(check_tensor(q, "q"));
+  CRU_TRY(check_tensor(k, "k"));
+  CRU_TRY(check_tensor(v, "v"));
+  CRU_TRY(check_tensor(o, "o"));
+  if (k->dtype != q->dtype || v->dtype != q->dtype)
+    return fail(CRU_EUNSUPPORTED, "q, k, v dtypes differ (%s, %s, %s)", dtype_name(q->dtype),
+                dtype_name(k->dtype), dtype_name(v->dtype));
+  if (q->dtype == CRU_F32 && o->dtype != CRU_F32)
+    return fail(CRU_EUNSUPPORTED, "fp32 inputs need an fp32 output");
+  if (k->B != q->B || k->H != q->H || k->D != q->D)
+    return fail(CRU_EINVAL, "k [%lld, %lld, %lld, %lld] does not match q [%lld, _, %lld, %lld]",
+                (long long)k->B, (long long)k->S, (long long)k->H, (long long)k->D,
+                (long long)q->B, (long long)q->H, (long long)q->D);
+  if (!same_shape(v, k)) return fail(CRU_EINVAL, "v shape differs from k");
+  if (!same_shape(o, q)) return fail(CRU_EINVAL, "o shape differs from q");
+  CRU_TRY(check_head_dim(q, "q"));
+  return CRU_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char* cru_status_str(int status) {
+  switch (status) {
+    case CRU_OK: return "CRU_OK";
+    case CRU_EINVAL: return "CRU_EINVAL";
+    case CRU_ENOTDIV: return "CRU_ENOTDIV";
+    case CRU_EUNSUPPORTED: return "CRU_EUNSUPPORTED";
+    case CRU_EDEVICE: return "CRU_EDEVICE";
+    case CRU_EWORKSPACE: return "CRU_EWORKSPACE";
+    case CRU_EHIP: return "CRU_EHIP";
+    default: return "CRU_UNKNOWN";
+  }
+}
+
+const char* cru_last_error(void) { return g_err; }
+
+int cru_abi_version(void) { return CRU_ABI_VERSION; }
+
+cru_status cru_attn_fwd_lse(const cru_tensor* q, const cru_tensor* k, const cru_tensor* v,
+                            const cru_tensor* o, const cru_lse* lse, float scale,
+                            hipStream_t stream) {
+  g_err[0] = '\0';
+  CRU_TRY(check_qkvo(q, k, v, o));
+  if (lse != nullptr) CRU_TRY(check_lse(lse, "lse", q->B, q->H, q->S));
+  float scale_log2 = 0.0f;
+  CRU_TRY(check_scale(scale, q->D, &scale_log2));
+  const int64_t nq = q->B * q->H * q->S;
+  if (nq == 0) return CRU_OK;
+  CRU_TRY(check_device(q->data, "q"));
+  CRU_TRY(check_device(k->data, "k"));
+  CRU_TRY(check_device(v->data, "v"));
+  CRU_TRY(check_device(o->data, "o"));
+  if (lse != nullptr) CRU_TRY(check_device(lse->data, "lse"));
+
+  cru::AttnArgs a = {};
+  fill_attn_views(a, q, k, v);
+  a.o = o->data;
+  a.o_sb = o->sb; a.o_ss = o->ss; a.o_sh = o->sh;
+  a.o_f32 = o->dtype == CRU_F32;
+  a.lse = lse ? lse->data : nullptr;
+  a.l_sb = lse ? lse->sb : 0;
+  a.l_sh = lse ? lse->sh : 0;
+  a.n_split = 1;
+  a.split_start[0] = 0;
+  a.split_start[1] = (int)k->S;
+  a.scale_log2 = scale_log2;
+  const hipError_t e = q->dtype == CRU_BF16 ? cru::launch_attn_bf16(a, stream)
+                                            : cru::launch_attn_f32(a, stream);
+  return hip_status(e, "attention launch");
+}
+
+cru_status cru_attn_merge_lse(int n, const cru_tensor* o_parts, const cru_lse* lse_parts,
+                              const cru_tensor* o, const cru_lse* lse, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (n < 1 || n > CRU_MAX_PARTS)
+    return fail(CRU_EINVAL, "n = %d parts, must be in [1, %d]", n, CRU_MAX_PARTS);
+  if (o_parts == nullptr || lse_parts == nullptr)
+    return fail(CRU_EINVAL, "o_parts / lse_parts is NULL");
+  const cru_tensor* p0 = &o_parts[0];
+  for (int c = 0; c < n; ++c) {
+    const cru_tensor* p = &o_parts[c];
+    CRU_TRY(check_tensor(p, "o_parts[c]"));
+    if (p->dtype != CRU_F32)
+      return fail(CRU_EUNSUPPORTED, "o_parts[%d] is %s; partial outputs are fp32", c,
+                  dtype_name(p->dtype));
+    if (!same_shape(p, p0)) return fail(CRU_EINVAL, "o_parts[%d] shape differs from o_parts[0]", c);
+    if (p->sb != p0->sb || p->ss != p0->ss || p->sh != p0->sh)
+      return fail(CRU_EINVAL, "o_parts[%d] strides differ from o_parts[0]", c);
+    CRU_TRY(check_lse(&lse_parts[c], "lse_parts[c]", p0->B, p0->H, p0->S));
+    if (lse_parts[c].sb != lse_parts[0].sb || lse_parts[c].sh != lse_parts[0].sh)
+      return fail(CRU_EINVAL, "lse_parts[%d] strides differ from lse_parts[0]", c);
+  }
+  CRU_TRY(check_head_dim(p0, "o_parts[0]"));
+  CRU_TRY(check_tensor(o, "o"));
+  if (!same_shape(o, p0)) return fail(CRU_EINVAL, "o shape differs from the parts");
+  if (lse != nullptr) CRU_TRY(check_lse(lse, "lse", p0->B, p0->H, p0->S));
+  if (p0->B * p0->H * p0->S == 0) return CRU_OK;
+  for (int c = 0; c < n; ++c) {
+    CRU_TRY(check_device(o_parts[c].data, "o_parts[c]"));
+    CRU_TRY(check_device(lse_parts[c].data, "lse_parts[c]"));
+  }
+  CRU_TRY(check_device(o->data, "o"));
+  if (lse != nullptr) CRU_TRY(check_device(lse->data, "lse"));
+
+  cru::MergeArgs a = {};
+  for (int c = 0; c < n; ++c) {
+    a.o_part[c] = static_cast<const float*>(o_parts[c].data);
+    a.l_part[c] = lse_parts[c].data;
+  }
+  a.p_sb = p0->sb; a.p_ss = p0->ss; a.p_sh = p0->sh;
+  a.pl_sb = lse_parts[0].sb; a.pl_sh = lse_parts[0].sh;
+  a.o = o->data;
+  a.o_sb = o->sb; a.o_ss = o->ss; a.o_sh = o->sh;
+  a.lse = lse ? lse->data : nullptr;
+  a.l_sb = lse ? lse->sb : 0;
+  a.l_sh = lse ? lse->sh : 0;
+  a.B = (int)p0->B; a.S = (int)p0->S; a.H = (int)p0->H; a.D = (int)p0->D;
+  a.n = n;
+  a.o_f32 = o->dtype == CRU_F32;
+  return hip_status(cru::launch_merge(a, stream), "merge launch");
+}
+
+cru_status cru_ring_workspace_bytes(const cru_tensor* q_share, int n_chunks, size_t* bytes) {
+  g_err[0] = '\0';
+  if (bytes == nullptr) return fail(CRU_EINVAL, "bytes is NULL");
+  CRU_TRY(check_tensor(q_share, "q_share"));
+  if (n_chunks < 1 || n_chunks > CRU_MAX_PARTS)
+    return fail(CRU_EINVAL, "n_chunks = %d, must be in [1, %d]", n_chunks, CRU_MAX_PARTS);
+  const size_t rows = (size_t)q_share->B * q_share->S * q_share->H;
+  *bytes = (size_t)n_chunks * (align256(rows * q_share->D * 4) + align256(rows * 4));
+  return CRU_OK;
+}
+
+cru_status cru_ring_chunk_bounds(int64_t S, int n, int anything, int64_t* starts) {
+  g_err[0] = '\0';
+  if (starts == nullptr) return fail(CRU_EINVAL, "starts is NULL");
+  if (n < 1 || n > CRU_MAX_PARTS)
+    return fail(CRU_EINVAL, "n = %d chunks, must be in [1, %d]", n, CRU_MAX_PARTS);
+  if (S < 0 || S > kMaxDim) return fail(CRU_EINVAL, "sequence length %lld out of range", (long long)S);
+  if (anything != 0 && anything != 1) return fail(CRU_EINVAL, "anything must be 0 or 1");
+  if (!anything && S % n != 0)
+    return fail(CRU_ENOTDIV,
+                "sequence length %lld is not divisible by ring degree %d "
+                "(set anything = 1 for Ring Anything)",
+                (long long)S, n);
+  const int64_t base = S / n, extra = S % n;
+  starts[0] = 0;
+  for (int c = 0; c < n; ++c) starts[c + 1] = starts[c] + base + (c < extra ? 1 : 0);
+  return CRU_OK;
+}
+
+cru_status cru_ring_emulate(const cru_tensor* q_share, const cru_tensor* k, const cru_tensor* v,
+                            int n_chunks, int anything, const int64_t* chunk_sizes, int fused,
+                            const cru_tensor* o, const cru_lse* lse, float scale,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = '\0';
+  CRU_TRY(check_qkvo(q_share, k, v, o));
+  if (lse != nullptr) CRU_TRY(check_lse(lse, "lse", q_share->B, q_share->H, q_share->S));
+  if (n_chunks < 1 || n_chunks > CRU_MAX_PARTS)
+    return fail(CRU_EINVAL, "n_chunks = %d, must be in [1, %d]", n_chunks, CRU_MAX_PARTS);
+  if (anything != 0 && anything != 1) return fail(CRU_EINVAL, "anything must be 0 or 1");
+  if (fused != 0 && fused != 1) return fail(CRU_EINVAL, "fused must be 0 or 1");
+  float scale_log2 = 0.0f;
+  CRU_TRY(check_scale(scale, q_share->D, &scale_log2));
+
+  const int64_t Skv = k->S;
+  int64_t start[CRU_MAX_PARTS + 1];
+  start[0] = 0;
+  if (chunk_sizes == nullptr) {
+    CRU_TRY(cru_ring_chunk_bounds(Skv, n_chunks, anything, start));
+  } else {
+    for (int c = 0; c < n_chunks; ++c) {
+      if (chunk_sizes[c] < 0) return fail(CRU_EINVAL, "chunk_sizes[%d] < 0", c);
+      start[c + 1] = start[c] + chunk_sizes[c];
+    }
+    if (start[n_chunks] != Skv)
+      return fail(CRU_EINVAL, "chunk sizes sum to %lld, K/V has %lld rows",
+                  (long long)start[n_chunks], (long long)Skv);
+    if (!anything)
+      for (int c = 1; c < n_chunks; ++c)
+        if (chunk_sizes[c] != chunk_sizes[0])
+          return fail(CRU_ENOTDIV, "unequal chunks need anything = 1 (Ring Anything)");
+  }
+
+  size_t need = 0;
+  CRU_TRY(cru_ring_workspace_bytes(q_share, n_chunks, &need));
+  if (need > 0 && workspace == nullptr) return fail(CRU_EWORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(CRU_EWORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(CRU_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+
+  const int64_t rows = q_share->B * q_share->H * q_share->S;
+  if (rows == 0) return CRU_OK;
+  CRU_TRY(check_device(q_share->data, "q_share"));
+  CRU_TRY(check_device(k->data, "k"));
+  CRU_TRY(check_device(v->data, "v"));
+  CRU_TRY(check_device(o->data, "o"));
+  if (lse != nullptr) CRU_TRY(check_device(lse->data, "lse"));
+  CRU_TRY(check_device(workspace, "workspace"));
+
+  // Partials in the workspace: n fp32 [B, Sq, H, D] outputs, then n [B, H, Sq] LSEs.
+  const int64_t B = q_share->B, Sq = q_share->S, H = q_share->H, D = q_share->D;
+  const size_t obytes = align256((size_t)rows * D * 4);
+  const size_t lbytes = align256((size_t)rows * 4);
+  char* ws = static_cast<char*>(workspace);
+  float* o_base = reinterpret_cast<float*>(ws);
+  float* l_base = reinterpret_cast<float*>(ws + n_chunks * obytes);
+
+  cru::AttnArgs a = {};
+  fill_attn_views(a, q_share, k, v);
+  a.o_sb = Sq * H * D; a.o_ss = H * D; a.o_sh = D;
+  a.l_sb = H * Sq; a.l_sh = Sq;
+  a.o_f32 = 1;
+  a.scale_log2 = scale_log2;
+  auto launch = q_share->dtype == CRU_BF16 ? cru::launch_attn_bf16 : cru::launch_attn_f32;
+  if (fused) {
+    a.o = o_base;
+    a.lse = l_base;
+    a.o_split_stride = (int64_t)(obytes / 4);
+    a.l_split_stride = (int64_t)(lbytes / 4);
+    a.n_split = n_chunks;
+    for (int c = 0; c <= n_chunks; ++c) a.split_start[c] = (int)start[c];
+    CRU_TRY(hip_status(launch(a, stream), "fused ring attention launch"));
+  } else {
+    a.n_split = 1;
+    for (int c = 0; c < n_chunks; ++c) {
+      a.o = reinterpret_cast<char*>(o_base) + c * obytes;
+      a.lse = reinterpret_cast<float*>(reinterpret_cast<char*>(l_base) + c * lbytes);
+      a.split_start[0] = (int)start[c];
+      a.split_start[1] = (int)start[c + 1];
+      CRU_TRY(hip_status(launch(a, stream), "ring step attention launch"));
+    }
+  }
+
+  cru::MergeArgs m = {};
+  for (int c = 0; c < n_chunks; ++c) {
+    m.o_part[c] = reinterpret_cast<const float*>(ws + c * obytes);
+    m.l_part[c] = reinterpret_cast<const float*>(reinterpret_cast<char*>(l_base) + c * lbytes);
+  }
+  m.p_sb = Sq * H * D; m.p_ss = H * D; m.p_sh = D;
+  m.pl_sb = H * Sq; m.pl_sh = Sq;
+  m.o = o->data;
+  m.o_sb = o->sb; m.o_ss = o->ss; m.o_sh = o->sh;
+  m.lse = lse ? lse->data : nullptr;
+  m.l_sb = lse ? lse->sb : 0;
+  m.l_sh = lse ? lse->sh : 0;
+  m.B = (int)B; m.S = (int)Sq; m.H = (int)H; m.D = (int)D;
+  m.n = n_chunks;
+  m.o_f32 = o->dtype == CRU_F32;
+  return hip_status(cru::launch_merge(m, stream), "ring merge launch");
+}
+
+static cru_status layout_common(int n, const cru_tensor* x, int P, const char* what,
+                                cru::LayoutArgs* a) {
+  if (n < 1 || n > 8) return fail(CRU_EINVAL, "%s: n = %d tensors, must be in [1, 8]", what, n);
+  if (x == nullptr) return fail(CRU_EINVAL, "%s: x is NULL", what);
+  for (int t = 0; t < n; ++t) {
+    CRU_TRY(check_tensor(&x[t], "x[t]"));
+    if (!same_shape(&x[t], &x[0]) || x[t].dtype != x[0].dtype)
+      return fail(CRU_EINVAL, "%s: x[%d] shape or dtype differs from x[0]", what, t);
+    if (x[t].sb != x[0].sb || x[t].ss != x[0].ss || x[t].sh != x[0].sh)
+      return fail(CRU_EINVAL, "%s: x[%d] strides differ from x[0]", what, t);
+  }
+  CRU_TRY(check_head_dim(&x[0], "x[0]"));
+  if (P < 1) return fail(CRU_EINVAL, "%s: P = %d must be >= 1", what, P);
+  if (x[0].H % P != 0)
+    return fail(CRU_ENOTDIV, "%s: head count %lld is not divisible by Ulysses degree %d", what,
+                (long long)x[0].H, P);
+  if (x[0].S % P != 0)
+    return fail(CRU_ENOTDIV, "%s: sequence length %lld is not divisible by Ulysses degree %d",
+                what, (long long)x[0].S, P);
+  a->sb = x[0].sb; a->ss = x[0].ss; a->sh = x[0].sh;
+  a->B = (int)x[0].B; a->S = (int)x[0].S; a->H = (int)x[0].H; a->D = (int)x[0].D;
+  a->P = P;
+  a->n = n;
+  a->elem_bytes = elem_bytes(x[0].dtype);
+  return CRU_OK;
+}
+
+cru_status cru_ulysses_seq2head(int n, const cru_tensor* x, void* const* y, int P,
+                                hipStream_t stream) {
+  g_err[0] = '\0';
+  cru::LayoutArgs a = {};
+  CRU_TRY(layout_common(n, x, P, "seq2head", &a));
+  if (y == nullptr) return fail(CRU_EINVAL, "seq2head: y is NULL");
+  const bool empty = (int64_t)a.B * a.S * a.H * a.D == 0;
+  for (int t = 0; t < n; ++t) {
+    if (!empty && y[t] == nullptr) return fail(CRU_EINVAL, "seq2head: y[%d] is NULL", t);
+    if (reinterpret_cast<uintptr_t>(y[t]) % 16 != 0)
+      return fail(CRU_EINVAL, "seq2head: y[%d] is not 16-byte aligned", t);
+  }
+  if (empty) return CRU_OK;
+  for (int t = 0; t < n; ++t) {
+    CRU_TRY(check_device(x[t].data, "x[t]"));
+    CRU_TRY(check_device(y[t], "y[t]"));
+    a.src[t] = x[t].data;
+    a.dst[t] = y[t];
+  }
+  a.dir = 0;
+  return hip_status(cru::launch_layout(a, stream), "seq2head launch");
+}
+
+cru_status cru_ulysses_head2seq(int n, const void* const* y, const cru_tensor* x, int P,
+                                hipStream_t stream) {
+  g_err[0] = '\0';
+  cru::LayoutArgs a = {};
+  CRU_TRY(layout_common(n, x, P, "head2seq", &a));
+  if (y == nullptr) return fail(CRU_EINVAL, "head2seq: y is NULL");
+  const bool empty = (int64_t)a.B * a.S * a.H * a.D == 0;
+  for (int t = 0; t < n; ++t) {
+    if (!empty && y[t] == nullptr) return fail(CRU_EINVAL, "head2seq: y[%d] is NULL", t);
+    if (reinterpret_cast<uintptr_t>(y[t]) % 16 != 0)
+      return fail(CRU_EINVAL, "head2seq: y[%d] is not 16-byte aligned", t);
+  }
+  if (empty) return CRU_OK;
+  for (int t = 0; t < n; ++t) {
+    CRU_TRY(check_device(y[t], "y[t]"));
+    CRU_TRY(check_device(x[t].data, "x[t]"));
+    a.src[t] = y[t];
+    a.dst[t] = x[t].data;
+  }
+  a.dir = 1;
+  return hip_status(cru::launch_layout(a, stream), "head2seq launch");
+}
+
+}  // extern "C"

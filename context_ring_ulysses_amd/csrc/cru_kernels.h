@@ -1,0 +1,69 @@
+// Internal launch interface between the host API (cru_api.cpp) and the HIP
+// kernels.  Arguments here are already validated; launchers only enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cru.h"
+
+namespace cru {
+
+// One attention launch: query rows [0, Sq) against key rows of `n_split`
+// consecutive key ranges [split_start[c], split_start[c+1]).  Split c writes
+// its (O, LSE) to o + c*o_split_stride and lse + c*l_split_stride.  With one
+// split this is a plain forward over keys [split_start[0], split_start[1]).
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;                 // may be null
+  int64_t q_sb, q_ss, q_sh;   // element strides
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t l_sb, l_sh;
+  int64_t o_split_stride;     // elements of o between splits
+  int64_t l_split_stride;     // elements of lse between splits
+  int B, H, Sq, D;
+  int o_f32;                  // 1: o is fp32, 0: o is bf16
+  int n_split;
+  float scale_log2;           // softmax scale times log2(e)
+  int split_start[CRU_MAX_PARTS + 1];
+};
+
+// Every part shares one set of strides (checked on the host).
+struct MergeArgs {
+  const float* o_part[CRU_MAX_PARTS];
+  const float* l_part[CRU_MAX_PARTS];
+  int64_t p_sb, p_ss, p_sh;
+  int64_t pl_sb, pl_sh;
+  void* o;
+  float* lse;                 // may be null
+  int64_t o_sb, o_ss, o_sh;
+  int64_t l_sb, l_sh;
+  int B, S, H, D;
+  int n;
+  int o_f32;
+};
+
+// Ulysses regrouping of up to 8 tensors of one shape and dtype.
+//   dir = 0: seq2head, strided x -> contiguous y [P, B, S, H/P, D]
+//   dir = 1: head2seq, contiguous y -> strided x
+struct LayoutArgs {
+  const void* src[8];
+  void* dst[8];
+  int64_t sb, ss, sh;         // strides of the [B, S, H, D] side
+  int B, S, H, D, P;
+  int n;
+  int elem_bytes;             // 2 or 4
+  int dir;
+};
+
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
+
+}  // namespace cru

@@ -1,0 +1,218 @@
+/*
+ * cru.h -- C ABI of the context-parallel attention library (libcru.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What it computes (sources are the pages this library follows):
+ *
+ *  - Softmax attention with its per-row log-sum-exp, non-causal and unmasked:
+ *    O = softmax(Q K^T * scale) V per (batch, head).  diffusers "Attention
+ *    backends" page, "Available backends" table: the default backend is
+ *    PyTorch's scaled_dot_product_attention, whose default scale is
+ *    1/sqrt(D).  diffusers "Parallelism" API page, ContextParallelConfig,
+ *    convert_to_fp32: ring attention carries the output *and* the LSE, in
+ *    fp32 by default.
+ *  - The LSE merge that folds partial results over disjoint key chunks into
+ *    the full result (the fold each ring step performs; same two pages).
+ *  - One ring rank's share: its query rows against every K/V chunk, folded
+ *    in ascending chunk order.  diffusers "Context parallelism" guide,
+ *    "Ring Attention" section (K/V blocks visited one after another) and
+ *    "Ring Anything Attention" section (chunks of unequal length).
+ *  - The sequence<->head regrouping of Ulysses attention.  Same guide,
+ *    "Ulysses Attention" section: the first all-to-all leaves each device
+ *    with every token of a subset of heads, the second regroups by token.
+ *
+ * Conventions shared by every entry point:
+ *  - All data pointers are device memory on the current HIP device, owned by
+ *    the caller.  The library never allocates, frees or synchronises; each
+ *    call only enqueues kernels on `stream` and returns.
+ *  - Tensors are described by cru_tensor: a [B, S, H, D] view with element
+ *    strides for b, s and h; d is contiguous (stride 1).  Strides must be
+ *    non-negative; the data pointer must be 16-byte aligned and the b/s/h
+ *    strides multiples of 8 elements (bf16) or 4 elements (fp32), so rows can
+ *    be moved 16 bytes at a time.
+ *  - The LSE is fp32 [B, H, S], natural log, described by cru_lse (s stride 1).
+ *  - Head dims: D = 64 or 128.
+ *  - All checks run on the host before anything is enqueued.  A failed check
+ *    returns a non-zero cru_status, enqueues nothing and leaves a message for
+ *    cru_last_error() (thread-local).  The checks follow the three classes of
+ *    the diffusers "Attention backends" page, "Checks" section: device
+ *    (CRU_EDEVICE), data type (CRU_EUNSUPPORTED) and shape (CRU_EINVAL), plus
+ *    the divisibility rules of the "Context parallelism" guide's variant
+ *    table (CRU_ENOTDIV).
+ *  - CRU_EHIP reports a HIP error raised while enqueueing.
+ *  - Calls that overlap on one stream are ordered by the stream; concurrent
+ *    calls on different streams must not write the same memory.
+ */
+#ifndef CRU_H
+#define CRU_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CRU_ABI_VERSION 1
+/* Most partial results one merge (or one ring share) may fold. */
+#define CRU_MAX_PARTS 64
+
+typedef enum {
+  CRU_OK = 0,
+  CRU_EINVAL = 1,        /* null pointer, bad shape or stride, size mismatch */
+  CRU_ENOTDIV = 2,       /* a divisibility rule of the variant is broken */
+  CRU_EUNSUPPORTED = 3,  /* dtype combination or head dim not implemented */
+  CRU_EDEVICE = 4,       /* a pointer is not device memory of the current device */
+  CRU_EWORKSPACE = 5,    /* workspace missing, misaligned or too small */
+  CRU_EHIP = 6           /* the HIP runtime reported an error */
+} cru_status;
+
+typedef enum { CRU_F32 = 0, CRU_BF16 = 1 } cru_dtype;
+
+/* A [B, S, H, D] tensor view.  Element (b, s, h, d) lives at
+ * data + (b*sb + s*ss + h*sh + d) elements of `dtype`. */
+typedef struct {
+  void*   data;
+  int32_t dtype;          /* cru_dtype */
+  int32_t reserved;       /* must be 0 */
+  int64_t B, S, H, D;
+  int64_t sb, ss, sh;
+} cru_tensor;
+
+/* Per-row LSE, fp32 [B, H, S]: element (b, h, s) at data + b*sb + h*sh + s. */
+typedef struct {
+  float*  data;
+  int64_t B, H, S;
+  int64_t sb, sh;
+} cru_lse;
+
+/*
+ * cru_attn_fwd_lse -- O = softmax(Q K^T * scale) V and LSE = log sum_j
+ * exp(q.k_j * scale), per batch, head and query row; non-causal, no mask.
+ *
+ *   q    [B, Sq, H, D]     bf16 or fp32
+ *   k, v [B, Skv, H, D]    same dtype as q
+ *   o    [B, Sq, H, D]     bf16 or fp32 for bf16 inputs; fp32 for fp32 inputs
+ *   lse  [B, H, Sq] fp32, or NULL when not wanted
+ *   scale  > 0, or 0 for 1/sqrt(D)
+ *
+ * bf16 inputs run on bf16 matrix cores with fp32 accumulation; P is rounded
+ * to bf16 (nearest even) before the P V product and O is rounded to nearest
+ * even when o is bf16.  fp32 inputs run in fp32 throughout.
+ * Skv = 0 gives O = 0 and LSE = -inf; Sq = 0 enqueues nothing.
+ * o must not overlap q, k or v.
+ */
+cru_status cru_attn_fwd_lse(const cru_tensor* q, const cru_tensor* k,
+                            const cru_tensor* v, const cru_tensor* o,
+                            const cru_lse* lse, float scale,
+                            hipStream_t stream);
+
+/*
+ * cru_attn_merge_lse -- combine n partial results over disjoint key sets:
+ *   LSE = M + log sum_c exp(LSE_c - M),  M = max_c LSE_c
+ *   O   = sum_c exp(LSE_c - LSE) * O_c, summed in ascending c.
+ * A part with LSE_c = -inf holds no keys and contributes nothing; rows where
+ * every part is empty give O = 0, LSE = -inf.
+ *
+ *   o_parts    host array of n fp32 [B, S, H, D] views, all the same shape
+ *              and strides
+ *   lse_parts  host array of n fp32 [B, H, S] LSE views, all the same strides
+ *   o          [B, S, H, D] bf16 or fp32
+ *   lse        [B, H, S] fp32, or NULL
+ *   1 <= n <= CRU_MAX_PARTS
+ * Outputs must not overlap the inputs.
+ */
+cru_status cru_attn_merge_lse(int n, const cru_tensor* o_parts,
+                              const cru_lse* lse_parts, const cru_tensor* o,
+                              const cru_lse* lse, hipStream_t stream);
+
+/*
+ * cru_ring_workspace_bytes -- bytes of device workspace cru_ring_emulate
+ * needs for a query share shaped like q_share cut into n_chunks chunks
+ * (n_chunks fp32 partial outputs and LSEs).  The same size serves both the
+ * step-wise and the fused schedule.
+ */
+cru_status cru_ring_workspace_bytes(const cru_tensor* q_share, int n_chunks,
+                                    size_t* bytes);
+
+/*
+ * cru_ring_chunk_bounds -- the split of S sequence rows into n consecutive
+ * chunks that cru_ring_emulate uses when chunk_sizes is NULL: chunk c is
+ * rows [starts[c], starts[c+1]).  The first S mod n chunks get one extra row
+ * (sizes differ by at most one).  With anything = 0, S must be divisible by
+ * n (CRU_ENOTDIV otherwise), as plain ring attention requires.  Host-only;
+ * starts is a host array of n + 1 entries.  Ring rank r's query share is
+ * chunk r of the same split.
+ */
+cru_status cru_ring_chunk_bounds(int64_t S, int n, int anything, int64_t* starts);
+
+/*
+ * cru_ring_emulate -- one ring rank's share on one device: the rank's query
+ * rows q_share against every K/V chunk, each chunk's fp32 partial (output,
+ * LSE) folded into o and lse in ascending chunk order.
+ *
+ *   q_share      [B, Sq, H, D] bf16 or fp32: the rank's query rows
+ *   k, v         [B, Skv, H, D], q's dtype: all chunks, back to back (what every
+ *                rank holds after the K/V all-gather)
+ *   n_chunks     ring degree, 1..CRU_MAX_PARTS
+ *   anything     0: Skv must split evenly (CRU_ENOTDIV otherwise);
+ *                1: any Skv ("Ring Anything": chunks may differ in length)
+ *   chunk_sizes  host array of n_chunks lengths summing to Skv, or NULL for
+ *                the near-equal split (the first Skv mod n chunks get one
+ *                extra row); with anything = 0 they must all be equal
+ *   fused        0: one attention launch per chunk (the ring's step order);
+ *                1: one launch over every (chunk, query tile, head)
+ *   o            [B, Sq, H, D] bf16 or fp32;  lse [B, H, Sq] fp32 or NULL
+ *   scale        as for cru_attn_fwd_lse
+ *   workspace    device memory of at least cru_ring_workspace_bytes(),
+ *                256-byte aligned, not overlapping any argument
+ * Empty chunks are allowed with anything = 1 and contribute nothing.
+ */
+cru_status cru_ring_emulate(const cru_tensor* q_share, const cru_tensor* k,
+                            const cru_tensor* v, int n_chunks, int anything,
+                            const int64_t* chunk_sizes, int fused,
+                            const cru_tensor* o, const cru_lse* lse,
+                            float scale, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * cru_ulysses_seq2head -- the first Ulysses all-to-all's net effect on one
+ * device, for n tensors in one launch:
+ *   y_t[p, b, s, j, d] = x_t[b, s, p*H/P + j, d],
+ * i.e. [B, S, H, D] -> [P, B, S, H/P, D]; group p holds every token of heads
+ * [p*H/P, (p+1)*H/P).  A bit-exact copy.
+ *
+ *   x   host array of n views, all the same shape and dtype (bf16 or fp32)
+ *   y   host array of n device pointers to contiguous [P, B, S, H/P, D]
+ *       buffers of that dtype, 16-byte aligned, not overlapping any x
+ *   1 <= n <= 8;  P >= 1 must divide H and S (CRU_ENOTDIV otherwise: the
+ *   sequence is sharded P ways before the exchange).
+ */
+cru_status cru_ulysses_seq2head(int n, const cru_tensor* x, void* const* y,
+                                int P, hipStream_t stream);
+
+/*
+ * cru_ulysses_head2seq -- the inverse regrouping (the second all-to-all):
+ *   x_t[b, s, p*H/P + j, d] = y_t[p, b, s, j, d].
+ *
+ *   y   host array of n device pointers to contiguous [P, B, S, H/P, D]
+ *   x   host array of n output views [B, S, H, D] (shape, dtype, strides)
+ *   same rules as cru_ulysses_seq2head.
+ */
+cru_status cru_ulysses_head2seq(int n, const void* const* y,
+                                const cru_tensor* x, int P,
+                                hipStream_t stream);
+
+/* Name of a status code (static storage). */
+const char* cru_status_str(int status);
+/* Message of the last failed call on this thread ("" if none). */
+const char* cru_last_error(void);
+/* CRU_ABI_VERSION of the built library. */
+int cru_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CRU_H */

@@ -1,0 +1,354 @@
+"""HIP path vs the fp64 oracle, through the C ABI (needs an MI355X).
+
+Tolerances: fp32 inputs 1e-5 (max abs, O and LSE); bf16 inputs 2e-2 on O and
+1e-3 on LSE; layout shuffles bit-exact.  Where several results are correct
+(a chunked sum rounds differently from an unchunked one), GPU results are
+compared with each other within the same bf16 tolerance; where the
+arithmetic is identical by construction (a head's attention does not depend
+on which other heads share the launch, the step-wise and fused ring
+schedules run the same per-chunk code) they are compared bit for bit.
+"""
+import functools
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import context_ring_ulysses_amd as cru
+import oracle
+from workloads import make_inputs, random_qkv, to_f64, workload
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_O = 2e-2
+TOL_LSE = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    cru.lib()
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def err(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    both_ninf = np.isneginf(a) & np.isneginf(b)
+    e = np.where(both_ninf, 0.0, np.abs(a - b))
+    assert not np.isnan(e).any(), "NaN in comparison"
+    return float(e.max()) if e.size else 0.0
+
+
+def cuda(*ts):
+    return [t.cuda() for t in ts]
+
+
+@functools.lru_cache(maxsize=2)
+def inputs(idx):
+    q, k, v = make_inputs(idx)
+    return (q, k, v), tuple(cuda(q, k, v))
+
+
+def sample_rows(S, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 63, 64, 127, 128, 129, S // 2, S - 2, S - 1]
+    rows = set(r for r in fixed if 0 <= r < S)
+    rows |= set(rng.choice(S, size=min(n, S), replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+def check_rows(o_gpu, l_gpu, q64, k64, v64, rows, tol_o, tol_l, what):
+    o_ref, l_ref = oracle.attention(q64[:, rows], k64, v64)
+    eo = err(to_f64(o_gpu)[:, rows], o_ref)
+    el = err(to_f64(l_gpu)[:, :, rows], l_ref)
+    say(f"  {what}: max|dO| = {eo:.3e}, max|dLSE| = {el:.3e} over {len(rows)} rows")
+    assert eo <= tol_o, f"{what}: O error {eo}"
+    assert el <= tol_l, f"{what}: LSE error {el}"
+
+
+# ------------------------------------------------------------ fp32 (workload 1)
+
+def test_fp32_tiny_full():
+    (q, k, v), (qd, kd, vd) = inputs(1)
+    say("tiny fp32 full forward", tuple(q.shape))
+    o, l = cru.attn_fwd_lse(qd, kd, vd)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v))
+    assert err(to_f64(o), o_ref) <= TOL_F32
+    assert err(to_f64(l), l_ref) <= TOL_F32
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("rank", [0, 1, 2, 3])
+def test_fp32_tiny_ring_share(rank, fused):
+    (q, k, v), (qd, kd, vd) = inputs(1)
+    N = workload(1).ring_degree
+    a, b = cru.ring_chunk_bounds(q.shape[1], N)[rank]
+    say(f"tiny fp32 ring share rank {rank} of {N}, fused={fused}")
+    o, l = cru.ring_emulate(qd[:, a:b], kd, vd, N, fused=fused)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.ring_share(to_f64(q), to_f64(k), to_f64(v), N, rank)
+    assert err(to_f64(o), o_ref) <= TOL_F32
+    assert err(to_f64(l), l_ref) <= TOL_F32
+
+
+# --------------------------------------------- bf16, small sizes, every element
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("D", [64, 128])
+def test_bf16_ragged_full(D, out_dtype):
+    # several query tiles and key tiles, with ragged tails on both
+    q, k, v = random_qkv(100 + D, B=2, Sq=300, Skv=517, H=3, D=D, gain=math.sqrt(3.0))
+    say(f"bf16 ragged D={D} out={out_dtype}")
+    o, l = cru.attn_fwd_lse(*cuda(q, k, v), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v))
+    eo, el = err(to_f64(o), o_ref), err(to_f64(l), l_ref)
+    say(f"  max|dO| = {eo:.3e}, max|dLSE| = {el:.3e}")
+    assert eo <= TOL_O and el <= TOL_LSE
+
+
+@pytest.mark.parametrize("shape", [(1, 10, 10, 8, 64), (1, 1, 1, 1, 128), (3, 1, 700, 2, 64),
+                                   (1, 129, 65, 5, 128), (2, 257, 129, 1, 64)])
+def test_bf16_odd_shapes(shape):
+    B, Sq, Skv, H, D = shape
+    q, k, v = random_qkv(7, B, Sq, Skv, H, D)
+    say("bf16 shape", shape)
+    o, l = cru.attn_fwd_lse(*cuda(q, k, v))
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v))
+    assert err(to_f64(o), o_ref) <= TOL_O
+    assert err(to_f64(l), l_ref) <= TOL_LSE
+
+
+def test_strided_views_and_scale():
+    # q, k, v as non-contiguous views ([B, H, S, D] storage) and an explicit scale
+    q, k, v = random_qkv(8, 2, 150, 190, 4, 128)
+    qd, kd, vd = (t.cuda().permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for t in (q, k, v))
+    assert qd.stride(1) == 128 and not qd.is_contiguous()
+    o, l = cru.attn_fwd_lse(qd, kd, vd, scale=0.05)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), scale=0.05)
+    assert err(to_f64(o), o_ref) <= TOL_O
+    assert err(to_f64(l), l_ref) <= TOL_LSE
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_degenerate_cases(dtype):
+    q, k, v = random_qkv(9, 1, 70, 1, 2, 64, dtype=dtype)
+    qd, kd, vd = cuda(q, k, v)
+    say("degenerate cases", dtype)
+    # one key: its weight is 1, so O = v_0 (up to the rounding of 1/l) and
+    # LSE = its score
+    o, l = cru.attn_fwd_lse(qd, kd, vd, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    v0 = to_f64(v.float().expand(1, 70, 2, 64))
+    assert err(to_f64(o), v0) <= 1e-6 * max(1.0, float(np.abs(v0).max()))
+    s = np.einsum("bihd,bjhd->bhi", to_f64(q), to_f64(k)) / 8.0
+    assert err(to_f64(l), s) <= (TOL_F32 if dtype == "f32" else TOL_LSE)
+    # no keys: O = 0, LSE = -inf
+    o, l = cru.attn_fwd_lse(qd, kd[:, :0], vd[:, :0], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert (o.cpu() == 0).all() and torch.isneginf(l.cpu()).all()
+    # no queries: nothing to do
+    o, l = cru.attn_fwd_lse(qd[:, :0], kd, vd)
+    torch.cuda.synchronize()
+    assert o.shape == (1, 0, 2, 64) and l.shape == (1, 2, 0)
+
+
+def test_constant_v_and_zero_k():
+    q, k, v = random_qkv(10, 1, 200, 300, 2, 128, gain=math.sqrt(3.0))
+    c = torch.randn(1, 1, 2, 128, generator=torch.Generator().manual_seed(0)).to(torch.bfloat16)
+    vc = c.expand(1, 300, 2, 128).contiguous()
+    o, _ = cru.attn_fwd_lse(*cuda(q, k, vc), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    # weights sum to 1: O = c up to the rounding of P to bf16
+    assert err(to_f64(o), np.broadcast_to(to_f64(c), o.shape)) <= 4e-3 * float(c.abs().max())
+    o, l = cru.attn_fwd_lse(*cuda(q, torch.zeros_like(k), v), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert err(to_f64(o), np.broadcast_to(to_f64(v).mean(1, keepdims=True), o.shape)) <= 1e-5
+    assert err(to_f64(l), np.full(l.shape, math.log(300))) <= 1e-5
+
+
+# --------------------------------------------------------------------- merge
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_merge_kernel(out_dtype):
+    g = torch.Generator().manual_seed(11)
+    n, shape = 5, (2, 333, 3, 128)
+    parts = [torch.randn(shape, generator=g) for _ in range(n)]
+    lses = [torch.randn(2, 3, 333, generator=g) * 4 for _ in range(n)]
+    lses[2][:, :, :50] = -float("inf")          # part 2 empty for some rows
+    for c in range(n):
+        lses[c][1, 2, 7] = -float("inf")        # a row with no keys at all
+        parts[c][1, 7, 2] = 0.0
+    o, l = cru.attn_merge_lse([p.cuda() for p in parts], [x.cuda() for x in lses],
+                              out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.merge_closed_form([p.double().numpy() for p in parts],
+                                            [x.double().numpy() for x in lses])
+    tol = TOL_F32 if out_dtype == torch.float32 else TOL_O
+    assert err(to_f64(o), o_ref) <= tol
+    assert err(to_f64(l), l_ref) <= TOL_F32
+    assert torch.isneginf(l[1, 2, 7]).item() and (o[1, 7, 2] == 0).all().item()
+
+
+# -------------------------------------------------------- layouts, bit-exact
+
+@pytest.mark.parametrize("idx", [2, 5])
+def test_ulysses_layouts_bit_exact(idx):
+    w = workload(idx)
+    (q, k, v), (qd, kd, vd) = inputs(idx)
+    P = w.ulysses_degree
+    say(f"seq2head/head2seq {w.name} P={P}")
+    ys = cru.ulysses_seq2head([qd, kd, vd], P)
+    torch.cuda.synchronize()
+    for y, x in zip(ys, (q, k, v)):
+        ref = oracle.seq2head(x.view(torch.int16).numpy(), P)
+        assert np.array_equal(y.cpu().view(torch.int16).numpy(), ref)
+    back = cru.ulysses_head2seq(ys, P)
+    torch.cuda.synchronize()
+    for b_, x in zip(back, (q, k, v)):
+        assert torch.equal(b_.cpu().view(torch.int16), x.view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_layout_strided_and_other_degrees(dtype):
+    g = torch.Generator().manual_seed(12)
+    big = torch.randn(2, 40, 12, 64, generator=g).to(dtype).cuda()
+    x = big[:, :, 4:, :]                       # [2, 40, 8, 64], strided over heads
+    for P in (1, 2, 4, 8):
+        y = cru.ulysses_seq2head(x, P)
+        torch.cuda.synchronize()
+        ref = oracle.seq2head(x.cpu().float().numpy(), P)
+        assert np.array_equal(y.cpu().float().numpy(), ref)
+        out = torch.zeros_like(big)
+        cru.ulysses_head2seq(y, P, out=out[:, :, 4:, :])
+        torch.cuda.synchronize()
+        assert torch.equal(out[:, :, 4:, :].cpu(), x.cpu())
+        assert (out[:, :, :4, :] == 0).all().item()   # nothing written outside the view
+
+
+# ------------------------------------------------- the five workloads, full size
+
+@pytest.mark.parametrize("idx", [2, 3, 4, 5])
+def test_workload_full_forward(idx):
+    w = workload(idx)
+    (q, k, v), (qd, kd, vd) = inputs(idx)
+    say(f"full forward {w.name} B={w.B} S={w.S} H={w.H} D={w.D}")
+    o, l = cru.attn_fwd_lse(qd, kd, vd)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all().item() and torch.isfinite(l).all().item()
+    check_rows(o, l, to_f64(q), to_f64(k), to_f64(v), sample_rows(w.S, seed=idx),
+               TOL_O, TOL_LSE, w.name)
+
+
+@pytest.mark.parametrize("idx", [2, 5])
+def test_ulysses_share_matches_full_forward_bitwise(idx):
+    w = workload(idx)
+    (q, k, v), (qd, kd, vd) = inputs(idx)
+    P = w.ulysses_degree
+    Hp = w.H // P
+    o_full, l_full = cru.attn_fwd_lse(qd, kd, vd)
+    qs, ks, vs = cru.ulysses_seq2head([qd, kd, vd], P)
+    o_groups = []
+    for p in range(P):
+        say(f"ulysses share {w.name} group {p} of {P}")
+        o_p, l_p = cru.attn_fwd_lse(qs[p], ks[p], vs[p])
+        torch.cuda.synchronize()
+        # a head's arithmetic does not depend on its neighbours: bit-identical
+        assert torch.equal(o_p, o_full[:, :, p * Hp:(p + 1) * Hp])
+        assert torch.equal(l_p, l_full[:, p * Hp:(p + 1) * Hp])
+        o_groups.append(o_p)
+    o_back = cru.ulysses_head2seq(torch.stack(o_groups), P)
+    torch.cuda.synchronize()
+    assert torch.equal(o_back, o_full)
+    # and the share itself against the oracle (group 0, sampled rows)
+    q0, k0, v0 = (oracle.seq2head(to_f64(t), P)[0] for t in (q, k, v))
+    check_rows(o_groups[0], l_full[:, :Hp], q0, k0, v0, sample_rows(w.S, 24, seed=idx),
+               TOL_O, TOL_LSE, f"{w.name} ulysses group 0")
+
+
+@pytest.mark.parametrize("rank", [0, 5, 7])
+def test_flux1024_ring_share(rank):
+    w = workload(3)
+    (q, k, v), (qd, kd, vd) = inputs(3)
+    N = w.ring_degree
+    a, b = cru.ring_chunk_bounds(w.S, N)[rank]
+    say(f"flux-1024 ring share rank {rank}: rows [{a}, {b}) x {N} chunks")
+    o_s, l_s = cru.ring_emulate(qd[:, a:b], kd, vd, N, fused=False)
+    o_f, l_f = cru.ring_emulate(qd[:, a:b], kd, vd, N, fused=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s, o_f) and torch.equal(l_s, l_f)   # same per-chunk code
+    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
+    rows = sample_rows(b - a, 32, seed=rank)
+    # the unchunked definition for the sampled rows of the share
+    o_ref, l_ref = oracle.attention(q64[:, a:b][:, rows], k64, v64)
+    assert err(to_f64(o_s)[:, rows], o_ref) <= TOL_O
+    assert err(to_f64(l_s)[:, :, rows], l_ref) <= TOL_LSE
+    # the oracle's own ring share for the sampled rows, folded chunk by chunk
+    o_ring, l_ring = oracle.chunked_attention(q64[:, a:b][:, rows], k64, v64, N)
+    assert err(to_f64(o_s)[:, rows], o_ring) <= TOL_O
+    assert err(to_f64(l_s)[:, :, rows], l_ring) <= TOL_LSE
+
+
+def test_flux1024_all_rows_chunked_merge():
+    """All 4608 query rows against 8 chunks, merged (the merge at full size)."""
+    w = workload(3)
+    (q, k, v), (qd, kd, vd) = inputs(3)
+    o_full, l_full = cru.attn_fwd_lse(qd, kd, vd)
+    o_c, l_c = cru.ring_emulate(qd, kd, vd, w.ring_degree, fused=True)
+    torch.cuda.synchronize()
+    eo = err(to_f64(o_c), to_f64(o_full))
+    el = err(to_f64(l_c), to_f64(l_full))
+    say(f"  chunked+merged vs unchunked (GPU): max|dO| = {eo:.3e}, max|dLSE| = {el:.3e}")
+    assert eo <= TOL_O and el <= TOL_LSE
+    check_rows(o_c, l_c, to_f64(q), to_f64(k), to_f64(v), sample_rows(w.S, 24, seed=30),
+               TOL_O, TOL_LSE, "flux-1024 chunked+merged")
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_ring_anything_uneven_chunks(fused):
+    w = workload(4)
+    (q, k, v), (qd, kd, vd) = inputs(4)
+    N = w.ring_degree
+    with pytest.raises(cru.CruNotDivisible):
+        cru.ring_emulate(qd, kd, vd, N)                 # plain ring refuses S % N != 0
+    say(f"ring anything S={w.S} N={N} fused={fused}")
+    o_c, l_c = cru.ring_emulate(qd, kd, vd, N, anything=True, fused=fused)
+    o_full, l_full = cru.attn_fwd_lse(qd, kd, vd)
+    torch.cuda.synchronize()
+    assert err(to_f64(o_c), to_f64(o_full)) <= TOL_O
+    assert err(to_f64(l_c), to_f64(l_full)) <= TOL_LSE
+    check_rows(o_c, l_c, to_f64(q), to_f64(k), to_f64(v), sample_rows(w.S, 24, seed=40),
+               TOL_O, TOL_LSE, "ring anything chunked+merged")
+    # rank 0's share: its 581 rows
+    a, b = cru.ring_chunk_bounds(w.S, N, anything=True)[0]
+    assert (a, b) == (0, 581)
+    o_r, l_r = cru.ring_emulate(qd[:, a:b], kd, vd, N, anything=True, fused=fused)
+    torch.cuda.synchronize()
+    assert err(to_f64(o_r), to_f64(o_c)[:, a:b]) <= TOL_O
+
+
+def test_ring_empty_and_explicit_chunks():
+    q, k, v = random_qkv(13, 1, 100, 90, 2, 128)
+    qd, kd, vd = cuda(q, k, v)
+    sizes = [0, 40, 0, 1, 49, 0]
+    o, l = cru.ring_emulate(qd, kd, vd, len(sizes), anything=True, chunk_sizes=sizes)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.chunked_attention(to_f64(q), to_f64(k), to_f64(v), len(sizes), sizes)
+    assert err(to_f64(o), o_ref) <= TOL_O and err(to_f64(l), l_ref) <= TOL_LSE
+
+
+def test_device_errors():
+    q, k, v = random_qkv(14, 1, 16, 16, 2, 64)
+    with pytest.raises(cru.CruDeviceError):
+        cru.attn_fwd_lse(q.cuda(), k, v.cuda())          # k left in host memory
