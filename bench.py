@@ -1,0 +1,302 @@
+"""Benchmark of the context-parallel attention hot path on one MI355X.
+
+One step is one pass of the whole path over the FLUX.1-dev 1024x1024 joint
+attention shape (B=1, H=24, S=4096+512=4608, D=128, bf16, synthetic inputs):
+
+  1. the full forward: attention with per-row LSE over all 4608 rows;
+  2. ring rank 0's share at ring degree 8: its 576 query rows against the
+     8 K/V chunks, one launch per chunk in ring order, then the fold;
+  3. the 8-way LSE merge over all 4608 rows (8 fp32 partials -> bf16 O);
+  4. Ulysses rank 0's share at degree 2: seq2head of Q, K, V, attention over
+     its 12 heads at full length, head2seq of the output.
+
+Inputs (and the merge's partials) are resident in HBM before timing starts.
+``value`` is the attention work of a step (4*B*H*Sq*Skv*D summed over parts
+1, 2 and 4) divided by the step time.  The JSON line also carries each
+part's own time, the attention kernel's roofline (achieved TFLOP/s from HIP
+events on its stream vs the bf16 dense peak), cold-cache bandwidth of the
+merge and layout kernels, and the fp64 oracle timed on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py --copy-calibration   # plain copy of known size, for counters
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak
+METRIC = "attention TFLOP/s and % bf16 MFMA peak at FLUX-1024 shape; merge GB/s"
+ATTN_SOURCE = os.path.join(ROOT, "context_ring_ulysses_amd", "csrc", "attn_fwd_bf16.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "attn_fwd_bf16_flux1024_counters.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def attn_flops(B, H, Sq, Skv, D):
+    return 4.0 * B * H * Sq * Skv * D
+
+
+def merge_bytes(n, B, S, H, D, out_bytes=2):
+    rows = B * S * H
+    return n * (rows * D * 4 + rows * 4) + rows * D * out_bytes + rows * 4
+
+
+def source_sha256(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def counters_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when it is missing or was taken on a different kernel source."""
+    if not os.path.exists(COUNTERS):
+        return None
+    kv = {}
+    for line in open(COUNTERS):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_sha256(ATTN_SOURCE):
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(budget_s=10.0, max_forwards=480):
+    """The fp64 oracle's full forward on FLUX-1024, one head at a time (heads
+    cycled) until about ``budget_s`` of host time is spent; TFLOP/s with the
+    same flop count as the GPU."""
+    import oracle
+    from workloads import make_inputs, to_f64, workload
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()
+                     if d.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    w = workload(3)
+    q, k, v = make_inputs(3)
+    done, spent = 0, 0.0
+    while done < max_forwards and spent < budget_s:
+        h = done % w.H
+        qh, kh, vh = (to_f64(t[:, :, h:h + 1]) for t in (q, k, v))
+        t0 = time.perf_counter()
+        oracle.attention(qh, kh, vh)
+        spent += time.perf_counter() - t0
+        done += 1
+    flops = attn_flops(1, done, w.S, w.S, w.D)
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"fp64 oracle full forward of FLUX-1024 (S=4608, D=128, all rows), "
+                      f"{done} single-head forwards (heads cycled), {spent:.1f} s"}
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    x = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cold-reps", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share on one GPU; runs on more than one GPU "
+              "are not part of this build (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import context_ring_ulysses_amd as cru
+    from workloads import make_inputs, workload
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workload(3)
+    B, S, H, D = w.B, w.S, w.H, w.D
+    N = w.ring_degree
+    P = 2
+    Hp = H // P
+    log(f"[bench] workload {w.name}: B={B} S={S} H={H} D={D} ring={N} ulysses={P}")
+    q, k, v = (t.to(dev) for t in make_inputs(3))
+
+    # outputs and the merge's partials, all resident before timing
+    o_full = torch.empty_like(q)
+    l_full = torch.empty(B, H, S, dtype=torch.float32, device=dev)
+    a0, b0 = cru.ring_chunk_bounds(S, N)[0]
+    q_share = q[:, a0:b0]
+    o_ring = torch.empty_like(q_share)
+    l_ring = torch.empty(B, H, b0 - a0, dtype=torch.float32, device=dev)
+    ws = torch.empty(cru.ring_workspace_bytes(q_share, N), dtype=torch.uint8, device=dev)
+    parts_o, parts_l = [], []
+    for (a, b) in cru.ring_chunk_bounds(S, N):
+        o_c, l_c = cru.attn_fwd_lse(q, k[:, a:b], v[:, a:b], out_dtype=torch.float32)
+        parts_o.append(o_c)
+        parts_l.append(l_c)
+    o_merge = torch.empty_like(q)
+    l_merge = torch.empty(B, H, S, dtype=torch.float32, device=dev)
+    ys = [torch.empty(P, B, S, Hp, D, dtype=q.dtype, device=dev) for _ in range(3)]
+    o_groups = torch.zeros(P, B, S, Hp, D, dtype=q.dtype, device=dev)
+    l_u = torch.empty(B, Hp, S, dtype=torch.float32, device=dev)
+    o_u = torch.empty_like(q)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(marks=None):
+        m = marks
+        if m: m[0].record(stream)
+        cru.attn_fwd_lse(q, k, v, out=o_full, lse=l_full)
+        if m: m[1].record(stream)
+        cru.ring_emulate(q_share, k, v, N, out=o_ring, lse=l_ring, workspace=ws)
+        if m: m[2].record(stream)
+        cru.attn_merge_lse(parts_o, parts_l, out=o_merge, lse=l_merge)
+        if m: m[3].record(stream)
+        cru.ulysses_seq2head([q, k, v], P, out=ys)
+        cru.attn_fwd_lse(ys[0][0], ys[1][0], ys[2][0], out=o_groups[0], lse=l_u)
+        cru.ulysses_head2seq(o_groups, P, out=o_u)
+        if m: m[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    marks = [[ev() for _ in range(5)] for _ in range(args.steps)]
+    t_start, t_end = ev(), ev()
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(marks[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    part_ms = {name: statistics.mean(m[j].elapsed_time(m[j + 1]) for m in marks)
+               for j, name in enumerate(["attn_full", "ring_share", "merge_all_rows", "ulysses_share"])}
+
+    f_full = attn_flops(B, H, S, S, D)
+    f_ring = attn_flops(B, H, b0 - a0, S, D)
+    f_uly = attn_flops(B, Hp, S, S, D)
+    step_flops = f_full + f_ring + f_uly
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    attn_tflops = f_full / (part_ms["attn_full"] * 1e-3) / 1e12
+    mbytes = merge_bytes(N, B, S, H, D)
+    merge_gbs = mbytes / (part_ms["merge_all_rows"] * 1e-3) / 1e9
+    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step; attn {part_ms['attn_full']:.3f} ms "
+        f"= {attn_tflops:.1f} TFLOP/s; merge {merge_gbs:.0f} GB/s")
+
+    # cold-cache bandwidth: reading 1 GiB between reps evicts L2 and the MALL
+    # (a read leaves clean lines, so no write-back lands in the timed kernel)
+    scrub = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def cold(fn, reps):
+        ts = []
+        for _ in range(reps):
+            torch.sum(scrub, dim=0, out=sink)
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return statistics.median(ts), min(ts)
+
+    med, mn = cold(lambda: cru.attn_merge_lse(parts_o, parts_l, out=o_merge, lse=l_merge),
+                   args.cold_reps)
+    cold_merge = {"workload": "flux-1024, 8 fp32 partials over all 4608 rows -> bf16 O + LSE",
+                  "bytes": mbytes, "ms_median": med, "ms_min": mn,
+                  "GB/s": mbytes / (med * 1e-3) / 1e9,
+                  "frac_hbm_peak": mbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    del parts_o, parts_l
+
+    wv = workload(5)
+    qv, kv_, vv = (t.to(dev) for t in make_inputs(5))
+    Pv = wv.ulysses_degree
+    ysv = [torch.empty(Pv, wv.B, wv.S, wv.H // Pv, wv.D, dtype=qv.dtype, device=dev)
+           for _ in range(3)]
+    ov = torch.empty_like(qv)
+    tbytes = qv.numel() * qv.element_size()
+    med1, mn1 = cold(lambda: cru.ulysses_seq2head([qv, kv_, vv], Pv, out=ysv), args.cold_reps)
+    med2, mn2 = cold(lambda: cru.ulysses_head2seq(ysv[0], Pv, out=ov), args.cold_reps)
+    cold_layout = {
+        "workload": "video-dit-4276 (B=2, S=4276, H=30, D=64, bf16), P=2",
+        "seq2head_qkv": {"bytes": 6 * tbytes, "ms_median": med1, "ms_min": mn1,
+                         "GB/s": 6 * tbytes / (med1 * 1e-3) / 1e9,
+                         "frac_hbm_peak": 6 * tbytes / (med1 * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "head2seq_o": {"bytes": 2 * tbytes, "ms_median": med2, "ms_min": mn2,
+                       "GB/s": 2 * tbytes / (med2 * 1e-3) / 1e9,
+                       "frac_hbm_peak": 2 * tbytes / (med2 * 1e-3) / 1e9 / PEAK_HBM_GBS}}
+    del qv, kv_, vv, ysv, ov, scrub, sink
+    torch.cuda.synchronize()
+
+    traffic = counters_traffic()
+    roofline = {"kernel": "attn_fwd_bf16 (full forward, FLUX-1024)", "bound": "mfma",
+                "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                "algorithmic_flops_per_launch": f_full,
+                "avg_launch_ms": part_ms["attn_full"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host cores")
+        cpu = cpu_baseline()
+        log(f"[bench] oracle: {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "flux-1024", "B": B, "H": H, "S": S, "D": D,
+                   "ring_degree": N, "ulysses_degree": P,
+                   "step": "full forward + ring rank-0 share (8 chunks, step-wise) + "
+                           "8-way merge over all rows + Ulysses rank-0 share (P=2)",
+                   "step_attention_flops": step_flops},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parts_ms": part_ms,
+        "attn_full_tflops": attn_tflops,
+        "attn_full_frac_bf16_peak": attn_tflops / PEAK_BF16_TFLOPS,
+        "ring_share_tflops": f_ring / (part_ms["ring_share"] * 1e-3) / 1e12,
+        "ulysses_share_tflops_incl_layouts": f_uly / (part_ms["ulysses_share"] * 1e-3) / 1e12,
+        "merge_all_rows_GB/s_in_step": merge_gbs,
+        "cold_merge": cold_merge,
+        "cold_layout": cold_layout,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -159,6 +159,26 @@ cru_status check_qkvo(const cru_tensor* q, const cru_tensor* k, const cru_tensor
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The kernels index threads, rows and 16-byte vectors with 32-bit integers.
+constexpr int64_t kMaxIndex = ((int64_t)1 << 31) - 4096;
+
+cru_status check_index_range(int64_t count, const char* what) {
+  if (count > kMaxIndex)
+    return fail(CRU_EINVAL, "%s: %lld work items exceed one call's 2^31 limit; split the call",
+                what, (long long)count);
+  return CRU_OK;
+}
+
+// Workgroups of the attention kernels: (splits x B x H x query tiles of 128 rows).
+cru_status check_attn_grid(int64_t n_split, const cru_tensor* q) {
+  return check_index_range(n_split * q->B * q->H * ((q->S + 127) / 128) * 256, "attention");
+}
+
+// Threads of the merge kernel: one per 4 elements of every row.
+cru_status check_merge_grid(const cru_tensor* t) {
+  return check_index_range(t->B * t->S * t->H * (t->D / 4), "merge");
+}
+
 }  // namespace
 
 extern "C" {
@@ -188,6 +208,7 @@ cru_status cru_attn_fwd_lse(const cru_tensor* q, const cru_tensor* k, const cru_
   if (lse != nullptr) CRU_TRY(check_lse(lse, "lse", q->B, q->H, q->S));
   float scale_log2 = 0.0f;
   CRU_TRY(check_scale(scale, q->D, &scale_log2));
+  CRU_TRY(check_attn_grid(1, q));
   const int64_t nq = q->B * q->H * q->S;
   if (nq == 0) return CRU_OK;
   CRU_TRY(check_device(q->data, "q"));
@@ -238,6 +259,7 @@ cru_status cru_attn_merge_lse(int n, const cru_tensor* o_parts, const cru_lse* l
   CRU_TRY(check_tensor(o, "o"));
   if (!same_shape(o, p0)) return fail(CRU_EINVAL, "o shape differs from the parts");
   if (lse != nullptr) CRU_TRY(check_lse(lse, "lse", p0->B, p0->H, p0->S));
+  CRU_TRY(check_merge_grid(p0));
   if (p0->B * p0->H * p0->S == 0) return CRU_OK;
   for (int c = 0; c < n; ++c) {
     CRU_TRY(check_device(o_parts[c].data, "o_parts[c]"));
@@ -306,6 +328,8 @@ cru_status cru_ring_emulate(const cru_tensor* q_share, const cru_tensor* k, cons
   if (fused != 0 && fused != 1) return fail(CRU_EINVAL, "fused must be 0 or 1");
   float scale_log2 = 0.0f;
   CRU_TRY(check_scale(scale, q_share->D, &scale_log2));
+  CRU_TRY(check_attn_grid(n_chunks, q_share));
+  CRU_TRY(check_merge_grid(q_share));
 
   const int64_t Skv = k->S;
   int64_t start[CRU_MAX_PARTS + 1];
@@ -414,6 +438,8 @@ static cru_status layout_common(int n, const cru_tensor* x, int P, const char* w
   if (x[0].S % P != 0)
     return fail(CRU_ENOTDIV, "%s: sequence length %lld is not divisible by Ulysses degree %d",
                 what, (long long)x[0].S, P);
+  CRU_TRY(check_index_range(x[0].B * x[0].S * x[0].H * x[0].D * elem_bytes(x[0].dtype) / 16 + 512,
+                            what));
   a->sb = x[0].sb; a->ss = x[0].ss; a->sh = x[0].sh;
   a->B = (int)x[0].B; a->S = (int)x[0].S; a->H = (int)x[0].H; a->D = (int)x[0].D;
   a->P = P;

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "cru.h"
+#include "fastdiv.h"
 
 namespace cru {
 
@@ -46,6 +47,7 @@ struct MergeArgs {
   int B, S, H, D;
   int n;
   int o_f32;
+  FastDiv div_s, div_h;       // set by launch_merge
 };
 
 // Ulysses regrouping of up to 8 tensors of one shape and dtype.
@@ -59,6 +61,7 @@ struct LayoutArgs {
   int n;
   int elem_bytes;             // 2 or 4
   int dir;
+  FastDiv div_h, div_s, div_hp;   // set by launch_layout
 };
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);

@@ -7,12 +7,15 @@
 // w_c = e^{LSE_c - M}:
 //   LSE = M + log sum_c w_c,    O = (sum_c w_c O_c) / (sum_c w_c),
 // which equals sum_c e^{LSE_c - LSE} O_c; the sums run over c in ascending
-// order.  Parts with LSE_c = -inf hold no keys (w_c = 0).
+// order.  Parts with LSE_c = -inf hold no keys (w_c = 0, their O_c unused).
 //
 // Memory-bound: each part's O row is read once, O and LSE written once.
-// One thread owns 4 consecutive elements of one row; rows are ordered
-// (b, h, s) with s fastest so the LSE reads and writes of a wave are
-// contiguous, and every O row is read as whole 16-byte vectors.
+// One thread owns VPT float4 groups of one row.  Rows are ordered (b, h, s)
+// with s fastest, so the LSE reads and writes of a wave are contiguous and
+// every O row is read as whole 16-byte vectors.  All of a thread's loads are
+// issued before the first use: the part loop is unrolled over a compile-time
+// bound with wave-uniform predicates, so nothing waits on an earlier load
+// to decide whether to issue the next.
 #include "cru_kernels.h"
 
 namespace cru {
@@ -23,81 +26,170 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
 
 constexpr int kThreads = 256;
-constexpr int kBatch = 8;   // parts whose loads are issued together
+constexpr int kBatch = 16;    // parts loaded at once by the generic kernel
+constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kLn2 = 0.693147180559945309f;
 
-template <bool OF32>
-__global__ void __launch_bounds__(kThreads) merge_kernel(const MergeArgs a) {
-  const int gpr = a.D >> 2;                       // float4 groups per row
-  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t row = gid / gpr;
-  const int g = (int)(gid - row * gpr);
-  const int64_t nrows = (int64_t)a.B * a.H * a.S;
-  if (row >= nrows) return;
-  const int s = (int)(row % a.S);
-  const int64_t bh = row / a.S;
-  const int h = (int)(bh % a.H);
-  const int b = (int)(bh / a.H);
+struct RowPos {
+  int b, h, s, g;
+  bool live;
+};
 
-  const int64_t loff = b * a.pl_sb + h * a.pl_sh + s;
-  const int64_t ooff = b * a.p_sb + (int64_t)s * a.p_ss + h * a.p_sh + 4 * g;
+template <int VPT>
+__device__ __forceinline__ RowPos row_pos(const MergeArgs& a) {
+  const int gpr = (a.D >> 2) / VPT;                      // threads per row (power of 2)
+  const uint32_t gid = blockIdx.x * kThreads + threadIdx.x;
+  const uint32_t row = gid >> __builtin_ctz(gpr);
+  RowPos p;
+  p.g = (int)(gid - row * gpr);
+  p.live = row < (uint32_t)a.B * a.H * a.S;
+  const uint32_t bh = fdiv(row, a.div_s);
+  p.s = (int)(row - bh * a.S);
+  p.b = (int)fdiv(bh, a.div_h);
+  p.h = (int)(bh - p.b * a.H);
+  return p;
+}
 
-  float M = -__builtin_inff();
-  for (int c = 0; c < a.n; ++c) M = fmaxf(M, a.l_part[c][loff]);
+template <int VPT, bool OF32>
+__device__ __forceinline__ void store_row(const MergeArgs& a, const RowPos& p,
+                                          const f32x4 (&acc)[VPT], float inv, float lse) {
+  const int64_t odst = p.b * a.o_sb + (int64_t)p.s * a.o_ss + p.h * a.o_sh + 4 * VPT * p.g;
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    if constexpr (OF32) {
+      f32x4 y = {acc[u][0] * inv, acc[u][1] * inv, acc[u][2] * inv, acc[u][3] * inv};
+      *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + odst + 4 * u) = y;
+    } else {
+      bf16x4 y = {(__bf16)(acc[u][0] * inv), (__bf16)(acc[u][1] * inv),
+                  (__bf16)(acc[u][2] * inv), (__bf16)(acc[u][3] * inv)};
+      *reinterpret_cast<bf16x4*>(static_cast<u16*>(a.o) + odst + 4 * u) = y;
+    }
+  }
+  if (p.g == 0 && a.lse != nullptr) a.lse[p.b * a.l_sb + p.h * a.l_sh + p.s] = lse;
+}
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+// n <= NMAX parts, everything in registers.
+template <int NMAX, int VPT, bool OF32>
+__global__ void __launch_bounds__(kThreads) merge_small(const MergeArgs a) {
+  const RowPos p = row_pos<VPT>(a);
+  if (!p.live) return;
+  const int64_t loff = p.b * a.pl_sb + p.h * a.pl_sh + p.s;
+  const int64_t ooff = p.b * a.p_sb + (int64_t)p.s * a.p_ss + p.h * a.p_sh + 4 * VPT * p.g;
+
+  float l[NMAX];
+  f32x4 x[NMAX][VPT];
+#pragma unroll
+  for (int c = 0; c < NMAX; ++c)
+    l[c] = c < a.n ? __builtin_nontemporal_load(a.l_part[c] + loff) : -__builtin_inff();
+#pragma unroll
+  for (int c = 0; c < NMAX; ++c)
+#pragma unroll
+    for (int u = 0; u < VPT; ++u)
+      x[c][u] = c < a.n ? __builtin_nontemporal_load(
+                              reinterpret_cast<const f32x4*>(a.o_part[c] + ooff) + u)
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+
+  float M = l[0];
+#pragma unroll
+  for (int c = 1; c < NMAX; ++c) M = fmaxf(M, l[c]);
+  f32x4 acc[VPT];
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
   float sum = 0.f;
   if (M != -__builtin_inff()) {
-    for (int c0 = 0; c0 < a.n; c0 += kBatch) {
-      f32x4 x[kBatch];
-      float w[kBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int c = c0 + u;
-        if (c < a.n) {
-          const float lc = a.l_part[c][loff];
-          w[u] = expf(lc - M);                  // 0 for an empty part
-          x[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (lc != -__builtin_inff()) x[u] = *reinterpret_cast<const f32x4*>(a.o_part[c] + ooff);
-        } else {
-          x[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-          w[u] = 0.f;
-        }
-      }
+    for (int c = 0; c < NMAX; ++c) {
+      const float w = __builtin_amdgcn_exp2f((l[c] - M) * kLog2e);   // 0 for an empty part
+      if (w > 0.f) {
+        sum += w;
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        sum += w[u];
-        acc[0] = __builtin_fmaf(w[u], x[u][0], acc[0]);
-        acc[1] = __builtin_fmaf(w[u], x[u][1], acc[1]);
-        acc[2] = __builtin_fmaf(w[u], x[u][2], acc[2]);
-        acc[3] = __builtin_fmaf(w[u], x[u][3], acc[3]);
+        for (int u = 0; u < VPT; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[u][e] = __builtin_fmaf(w, x[c][u][e], acc[u][e]);
       }
     }
   }
   const float inv = sum > 0.f ? 1.0f / sum : 0.f;
-  const int64_t odst = b * a.o_sb + (int64_t)s * a.o_ss + h * a.o_sh + 4 * g;
-  if constexpr (OF32) {
-    f32x4 y = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-    *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + odst) = y;
-  } else {
-    bf16x4 y = {(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv), (__bf16)(acc[2] * inv),
-                (__bf16)(acc[3] * inv)};
-    *reinterpret_cast<bf16x4*>(static_cast<u16*>(a.o) + odst) = y;
+  const float lse = sum > 0.f ? M + __builtin_amdgcn_logf(sum) * kLn2 : -__builtin_inff();
+  store_row<VPT, OF32>(a, p, acc, inv, lse);
+}
+
+// Any n: a first pass over the LSEs for the max, then batches of kBatch parts.
+template <bool OF32>
+__global__ void __launch_bounds__(kThreads) merge_many(const MergeArgs a) {
+  const RowPos p = row_pos<1>(a);
+  if (!p.live) return;
+  const int64_t loff = p.b * a.pl_sb + p.h * a.pl_sh + p.s;
+  const int64_t ooff = p.b * a.p_sb + (int64_t)p.s * a.p_ss + p.h * a.p_sh + 4 * p.g;
+
+  float M = -__builtin_inff();
+  for (int c0 = 0; c0 < a.n; c0 += kBatch) {
+    float l[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      l[u] = c0 + u < a.n ? a.l_part[c0 + u][loff] : -__builtin_inff();
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) M = fmaxf(M, l[u]);
   }
-  if (g == 0 && a.lse != nullptr)
-    a.lse[b * a.l_sb + h * a.l_sh + s] = sum > 0.f ? M + logf(sum) : -__builtin_inff();
+  f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+  float sum = 0.f;
+  if (M != -__builtin_inff()) {
+    for (int c0 = 0; c0 < a.n; c0 += kBatch) {
+      float l[kBatch];
+      f32x4 x[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const bool in = c0 + u < a.n;
+        l[u] = in ? a.l_part[c0 + u][loff] : -__builtin_inff();
+        x[u] = in ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.o_part[c0 + u] + ooff))
+                  : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const float w = __builtin_amdgcn_exp2f((l[u] - M) * kLog2e);
+        if (w > 0.f) {
+          sum += w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[0][e] = __builtin_fmaf(w, x[u][e], acc[0][e]);
+        }
+      }
+    }
+  }
+  const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+  const float lse = sum > 0.f ? M + __builtin_amdgcn_logf(sum) * kLn2 : -__builtin_inff();
+  store_row<1, OF32>(a, p, acc, inv, lse);
+}
+
+template <int NMAX, bool OF32>
+hipError_t launch_small(const MergeArgs& a, hipStream_t stream) {
+  constexpr int VPT = 1;
+  const int64_t threads = (int64_t)a.B * a.H * a.S * (a.D / 4 / VPT);
+  const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL((merge_small<NMAX, VPT, OF32>), dim3(blocks), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <bool OF32>
+hipError_t launch_of(const MergeArgs& a, hipStream_t stream) {
+  if (a.n <= 2) return launch_small<2, OF32>(a, stream);
+  if (a.n <= 4) return launch_small<4, OF32>(a, stream);
+  if (a.n <= 8) return launch_small<8, OF32>(a, stream);
+  if (a.n <= 16) return launch_small<16, OF32>(a, stream);
+  const int64_t threads = (int64_t)a.B * a.H * a.S * (a.D / 4);
+  const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL((merge_many<OF32>), dim3(blocks), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
-  const int64_t threads = (int64_t)a.B * a.H * a.S * (a.D / 4);
-  if (threads == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
-  if (a.o_f32)
-    hipLaunchKernelGGL(merge_kernel<true>, dim3(blocks), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(merge_kernel<false>, dim3(blocks), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+hipError_t launch_merge(const MergeArgs& args, hipStream_t stream) {
+  const int64_t rows = (int64_t)args.B * args.H * args.S;
+  if (rows == 0) return hipSuccess;
+  MergeArgs a = args;
+  a.div_s = make_fastdiv((uint32_t)a.S);
+  a.div_h = make_fastdiv((uint32_t)a.H);
+  return a.o_f32 ? launch_of<true>(a, stream) : launch_of<false>(a, stream);
 }
 
 }  // namespace cru

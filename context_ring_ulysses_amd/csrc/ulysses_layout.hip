@@ -8,10 +8,11 @@
 // The [B, S, H, D] side may be strided (d contiguous); the [P, B, S, Hp, D]
 // side is contiguous.  Pure bit-exact copies, moved 16 bytes at a time.
 //
-// Memory-bound.  A workgroup owns a run of consecutive tokens of one batch
-// of one tensor; each (token, head) row of D elements is a contiguous run on
-// both sides, and the Hp rows of one group are contiguous on the y side, so
-// every wave reads and writes whole contiguous runs.
+// Memory-bound.  Vectors are numbered in [B, S, H, D] order, so a wave reads
+// (or writes) whole (token, head) rows of the strided side, and the Hp rows
+// of one group that follow each other are one contiguous run on the packed
+// side.  The index decomposition uses multiply-high division by the
+// invariant H, S and Hp; a thread issues all its loads before its stores.
 #include "cru_kernels.h"
 
 namespace cru {
@@ -20,50 +21,61 @@ namespace {
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
+constexpr int kNV = 2;    // vectors per thread
 
-template <int VPR>   // 16-byte vectors per (token, head) row
-__global__ void __launch_bounds__(kThreads) layout_kernel(const LayoutArgs a, int tokens_per_block) {
-  const int t = blockIdx.z;                       // tensor
-  const int b = blockIdx.y;
-  const int s0 = blockIdx.x * tokens_per_block;
-  const int ntok = min(tokens_per_block, a.S - s0);
+template <int VPR>   // 16-byte vectors per (token, head) row: 8, 16 or 32
+__global__ void __launch_bounds__(kThreads) layout_kernel(const LayoutArgs a) {
+  const char* __restrict__ src = static_cast<const char*>(a.src[blockIdx.y]);
+  char* __restrict__ dst = static_cast<char*>(a.dst[blockIdx.y]);
+  const uint32_t total = (uint32_t)a.B * a.S * a.H * VPR;
   const int Hp = a.H / a.P;
   const int vec_elems = 16 / a.elem_bytes;
-  const char* src = static_cast<const char*>(a.src[t]);
-  char* dst = static_cast<char*>(a.dst[t]);
-  const int work = ntok * a.H * VPR;
-  for (int u = threadIdx.x; u < work; u += kThreads) {
-    const int dv = u % VPR;                       // VPR is a power of two
-    const int rowi = u / VPR;
-    const int h = rowi % a.H;
-    const int s = s0 + rowi / a.H;
-    const int p = h / Hp;
+  const uint32_t base = blockIdx.x * (kThreads * kNV) + threadIdx.x;
+
+  u32x4 v[kNV];
+  int64_t to[kNV];
+#pragma unroll
+  for (int i = 0; i < kNV; ++i) {
+    const uint32_t g = base + i * kThreads;
+    const uint32_t row = g / VPR;
+    const int dv = (int)(g % VPR);
+    const uint32_t tok = fdiv(row, a.div_h);
+    const int h = (int)(row - tok * a.H);
+    const int b = (int)fdiv(tok, a.div_s);
+    const int s = (int)(tok - (uint32_t)b * a.S);
+    const int p = (int)fdiv((uint32_t)h, a.div_hp);
     const int j = h - p * Hp;
-    const int64_t strided = (int64_t)b * a.sb + (int64_t)s * a.ss + (int64_t)h * a.sh +
-                            (int64_t)dv * vec_elems;
-    const int64_t packed = ((((int64_t)p * a.B + b) * a.S + s) * Hp + j) * a.D +
-                           (int64_t)dv * vec_elems;
-    const int64_t from = (a.dir == 0 ? strided : packed) * a.elem_bytes;
-    const int64_t to = (a.dir == 0 ? packed : strided) * a.elem_bytes;
-    *reinterpret_cast<u32x4*>(dst + to) = *reinterpret_cast<const u32x4*>(src + from);
+    const int64_t strided = ((int64_t)b * a.sb + (int64_t)s * a.ss + (int64_t)h * a.sh +
+                             (int64_t)dv * vec_elems) * a.elem_bytes;
+    const int64_t packed = (((((int64_t)p * a.B + b) * a.S + s) * Hp + j) * a.D +
+                            (int64_t)dv * vec_elems) * a.elem_bytes;
+    const int64_t from = a.dir == 0 ? strided : packed;
+    to[i] = a.dir == 0 ? packed : strided;
+    v[i] = u32x4{0u, 0u, 0u, 0u};
+    if (g < total) v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + from));
   }
+#pragma unroll
+  for (int i = 0; i < kNV; ++i)
+    if (base + i * kThreads < total)
+      __builtin_nontemporal_store(v[i], reinterpret_cast<u32x4*>(dst + to[i]));
 }
 
 template <int VPR>
 hipError_t launch_vpr(const LayoutArgs& a, hipStream_t stream) {
-  // about 2048 vectors per workgroup
-  const int per_token = a.H * VPR;
-  int tpb = 2048 / per_token;
-  if (tpb < 1) tpb = 1;
-  const unsigned gx = (unsigned)((a.S + tpb - 1) / tpb);
-  hipLaunchKernelGGL(layout_kernel<VPR>, dim3(gx, a.B, a.n), dim3(kThreads), 0, stream, a, tpb);
+  const uint64_t total = (uint64_t)a.B * a.S * a.H * VPR;
+  const unsigned gx = (unsigned)((total + kThreads * kNV - 1) / (kThreads * kNV));
+  hipLaunchKernelGGL(layout_kernel<VPR>, dim3(gx, a.n), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
-  if ((int64_t)a.B * a.S * a.H * a.D == 0 || a.n == 0) return hipSuccess;
+hipError_t launch_layout(const LayoutArgs& args, hipStream_t stream) {
+  if ((int64_t)args.B * args.S * args.H * args.D == 0 || args.n == 0) return hipSuccess;
+  LayoutArgs a = args;
+  a.div_h = make_fastdiv((uint32_t)a.H);
+  a.div_s = make_fastdiv((uint32_t)a.S);
+  a.div_hp = make_fastdiv((uint32_t)(a.H / a.P));
   const int vpr = a.D * a.elem_bytes / 16;
   switch (vpr) {
     case 8: return launch_vpr<8>(a, stream);

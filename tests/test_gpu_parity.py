@@ -180,25 +180,29 @@ def test_constant_v_and_zero_k():
 
 # --------------------------------------------------------------------- merge
 
+@pytest.mark.parametrize("n", [1, 2, 5, 8, 13, 17, 40])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_merge_kernel(out_dtype):
-    g = torch.Generator().manual_seed(11)
-    n, shape = 5, (2, 333, 3, 128)
+def test_merge_kernel(out_dtype, n):
+    g = torch.Generator().manual_seed(11 + n)
+    shape = (2, 333, 3, 128) if n <= 8 else (1, 77, 2, 64)
     parts = [torch.randn(shape, generator=g) for _ in range(n)]
-    lses = [torch.randn(2, 3, 333, generator=g) * 4 for _ in range(n)]
-    lses[2][:, :, :50] = -float("inf")          # part 2 empty for some rows
+    B, S, H, _ = shape
+    lses = [torch.randn(B, H, S, generator=g) * 4 for _ in range(n)]
+    lses[n // 2][:, :, :50] = -float("inf")     # one part empty for some rows
+    parts[n // 2][:, :50] = float("nan")        # ... whose O must then be ignored
     for c in range(n):
-        lses[c][1, 2, 7] = -float("inf")        # a row with no keys at all
-        parts[c][1, 7, 2] = 0.0
+        lses[c][B - 1, H - 1, 7] = -float("inf")   # a row with no keys at all
+        parts[c][B - 1, 7, H - 1] = 0.0
     o, l = cru.attn_merge_lse([p.cuda() for p in parts], [x.cuda() for x in lses],
                               out_dtype=out_dtype)
     torch.cuda.synchronize()
-    o_ref, l_ref = oracle.merge_closed_form([p.double().numpy() for p in parts],
-                                            [x.double().numpy() for x in lses])
+    ref_parts = [p.double().numpy() for p in parts]
+    ref_parts[n // 2] = np.nan_to_num(ref_parts[n // 2])   # the oracle weights them by 0
+    o_ref, l_ref = oracle.merge_closed_form(ref_parts, [x.double().numpy() for x in lses])
     tol = TOL_F32 if out_dtype == torch.float32 else TOL_O
     assert err(to_f64(o), o_ref) <= tol
     assert err(to_f64(l), l_ref) <= TOL_F32
-    assert torch.isneginf(l[1, 2, 7]).item() and (o[1, 7, 2] == 0).all().item()
+    assert torch.isneginf(l[B - 1, H - 1, 7]).item() and (o[B - 1, 7, H - 1] == 0).all().item()
 
 
 # -------------------------------------------------------- layouts, bit-exact
