@@ -14,8 +14,11 @@
 // Work decomposition
 //   workgroup = 4 waves = one tile of 128 query rows of one (split, b, h);
 //   wave      = 32 query rows; lane (i = lane%32, half = lane/32).
-//   Key tiles of BC = 8192/D keys are staged in LDS, double buffered:
-//   K row-major (rows permuted, below), V transposed (V^T[d][key]).
+//   Key tiles of 64 keys go from global memory straight into LDS (buffer
+//   loads with the LDS destination bit: 64 lanes write 1 KiB contiguously,
+//   each lane choosing its 16-byte source), so no registers or VALU work
+//   stage them.  Both K and V are kept row-major in LDS, XOR-swizzled at
+//   16-byte granularity so the reads below hit distinct banks.
 //
 // The contraction is written as S^T = K Q^T with v_mfma_f32_32x32x16_bf16:
 // A = 32 keys x 16 dims of K (from LDS), B = 16 dims x 32 queries of Q^T
@@ -25,21 +28,38 @@
 // query row: the running max, the sum and the O rescale factor are per-lane
 // scalars, and only the two halves of a row need one exchange per tile.
 //
-// O^T = V^T P^T then uses A = 32 dims x 16 keys of V^T (LDS) and B = P^T,
-// which the lane already holds in its S^T registers.  For registers 0..7
-// (and 8..15) of a 32-key block to be the B operand of one MFMA, the keys they
-// hold must be 8 consecutive keys per half.  Register r of half h holds MFMA
-// row rho = 8*(r/4) + 4*h + r%4; storing key j of the tile in LDS row pi(j),
+// O^T = V^T P^T then uses A = 32 dims x 16 keys of V^T and B = P^T, which the
+// lane already holds in its S^T registers.  For registers 0..7 (and 8..15)
+// of a 32-key block to be the B operand of one MFMA, the keys they hold must
+// be 8 consecutive keys per half.  Register r of half h holds MFMA row
+// rho = 8*(r/4) + 4*h + r%4; storing key j of the tile in LDS row pi(j),
 // with pi swapping bits 2 and 3, makes that row hold key
 //   16*(r/8) + 8*h + r%8,
-// so half h of MFMA #(r/8) holds keys 16*(r/8) + 8*h + 0..7: one 16-byte
-// read of V^T.  Softmax is invariant to the order of keys, so the permutation
-// only has to be the same for K and V, which it is by construction.
+// so half h of MFMA #(r/8) holds keys 16*(r/8) + 8*h + 0..7.  Softmax is
+// invariant to the order of keys, so the permutation only has to be the same
+// for K and V, which it is by construction.  The A operand of V^T (row d,
+// 8 consecutive keys per lane) is read from row-major V with two
+// ds_read_b64_tr_b16: within a group of 16 lanes that instruction hands lane
+// j element 16e + j of the 16 x 4 block the lanes point at, so pointing lane
+// i at V[key0 + i/4][d0 + 4*(i%4) ..] gives lane j the 4 keys
+// key0 .. key0+3 of column d0 + j.
 //
-// Rescaling is lazy: the running max m (in log2 units) only moves when some
-// row's tile max exceeds it by more than kTau; otherwise P = 2^(x - m) may
-// reach 2^kTau, which fp32 sums and bf16 P hold exactly as well as values
-// below 1.  The final O / l and LSE = (m + log2 l) ln 2 are exact either way.
+// Software pipeline.  K and V have two LDS buffers each, one tile apart: in
+// the iteration for tile t the waves compute S^T of tile t (K buffer t%2)
+// and the P V product of tile t-1 (V buffer (t-1)%2), while the loads of K of
+// tile t+1 and V of tile t fill the other two buffers.  One barrier per tile
+// separates them.  The P V product of tile t-1 does not depend on tile t, so
+// it keeps the matrix cores busy while the vector unit computes tile t's
+// exponentials.  Global loads go through buffer descriptors built per tile
+// whose range ends at the last valid key row: rows past it read as zero
+// with no per-load bounds arithmetic.
+//
+// The running max m is kept in log2 units (scores times scale*log2(e)), so
+// P = 2^(x - m) <= 1 is one FMA and one v_exp_f32 per score.  The rescale of
+// O by 2^(m_old - m_new) is applied every tile without a branch (it is an
+// exact multiply by 1 when the max does not move), which keeps each tile's
+// instructions in one block for the scheduler.  The row sum l adds the fp32
+// P; only the P V product sees P rounded to bf16.
 #include "cru_kernels.h"
 
 namespace cru {
@@ -49,52 +69,90 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16;
 
 constexpr int kThreads = 256;
-constexpr float kTau = 8.0f;
 constexpr float kLn2 = 0.693147180559945309f;
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
+constexpr int kWaitVmem = 0x0F70;        // s_waitcnt vmcnt(0), other counters not waited
 
 template <int D>
 struct Tile {
-  static constexpr int BC = 8192 / D;          // keys per tile
+  static constexpr int BC = 64;                // keys per tile
   static constexpr int BM = 128;               // query rows per workgroup
-  static constexpr int KP = D + 8;             // LDS pitch of a K row (elements)
-  static constexpr int VP = BC + 8;            // LDS pitch of a V^T row
-  static constexpr int K_LDS = BC * KP;
-  static constexpr int V_LDS = D * VP;
-  static constexpr int STAGE = K_LDS + V_LDS;  // one buffer
+  static constexpr int RB = 2 * D;             // bytes per K or V row in LDS
+  static constexpr int KCH = D / 8;            // 16-byte chunks per row
   static constexpr int NJ = BC / 32;           // 32-key blocks per tile
   static constexpr int NK = D / 16;            // 16-wide steps of the QK^T contraction
   static constexpr int ND = D / 32;            // 32-wide blocks of O columns
-  static constexpr int KCH = D / 8;            // 16-byte chunks per row
-  static constexpr int KLOADS = BC * KCH / kThreads;
-  static constexpr int VJG = BC / 4;           // groups of 4 keys for the V transpose
-  static_assert(KLOADS * kThreads == BC * KCH, "tile must split evenly");
-  static_assert(VJG * KCH == kThreads, "one 4-key x 8-dim block per thread");
+  static constexpr int TILE_BYTES = BC * RB;   // one K or V tile
+  static constexpr int NLOAD = TILE_BYTES / (kThreads * 16);   // 16-byte loads per thread
+  static_assert(NLOAD * kThreads * 16 == TILE_BYTES, "tile must split evenly");
+  // K row R (LDS row, holding key key_row(R)) keeps logical chunk c at
+  // physical chunk c ^ kx(R): rows read together by one 16-lane group of the
+  // QK^T operand fetch land on 16 distinct 16-byte bank groups.
+  static __device__ __forceinline__ int kx(int R) {
+    return D == 128 ? (R & 15) : ((R >> 1) & 7);
+  }
+  // V row (key) k keeps logical chunk c at c ^ vx(k): the 4 keys x 64 bytes
+  // one transposing read fetches per half-wave land on distinct banks.
+  static __device__ __forceinline__ int vx(int k) {
+    return D == 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
+  }
 };
+
+struct NotFirst { static constexpr bool value = false; };
+struct First { static constexpr bool value = true; };
+struct NotLast { static constexpr bool value = false; };
+struct Last { static constexpr bool value = true; };
 
 __device__ __forceinline__ int key_row(int j) {
   // swap bits 2 and 3 of the key index (an involution)
   return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
 }
 
-__device__ __forceinline__ u32x4 ld16(const u16* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
-
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) {
   return __builtin_bit_cast(bf16x8, x);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 lds_read16(const char* base, int byte_off) {
+  return *reinterpret_cast<const u32x4*>(base + byte_off);
+}
+
+__device__ __forceinline__ v4i16 lds_read_tr(const char* base, int byte_off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(base + byte_off));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const u16* base, int64_t row0,
+                                                           int64_t row_stride, int nrows, int cap) {
+  // rows [row0, row0 + min(nrows, cap)) of a strided [rows, D] bf16 matrix;
+  // the host guarantees cap * row_stride * 2 < 2^31
+  const u16* p = base + row0 * row_stride;
+  const int n = nrows < cap ? nrows : cap;
+  const int bytes = n > 0 ? (int)(n * row_stride * 2) : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(p), (short)0, bytes, kRsrcWord3);
 }
 
 template <int D, bool OF32>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_bf16_kernel(const AttnArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  // The body is compiled for the device only; the host pass needs just the
+  // signature for the launch stub (it cannot type-check the gfx950 LDS
+  // builtins used below).
   using T = Tile<D>;
-  __shared__ __attribute__((aligned(16))) u16 lds[2 * T::STAGE];
+  __shared__ __attribute__((aligned(1024))) char kbuf0[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[T::TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -122,17 +180,19 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
   const int kv1 = a.split_start[split + 1];
 
   const u16* qg = static_cast<const u16*>(a.q) + b * a.q_sb + h * a.q_sh;
-  const u16* kg = static_cast<const u16*>(a.k) + b * a.k_sb + h * a.k_sh;
-  const u16* vg = static_cast<const u16*>(a.v) + b * a.v_sb + h * a.v_sh;
+  const u16* kg = static_cast<const u16*>(a.k) + b * a.k_sb + h * a.k_sh + kv0 * a.k_ss;
+  const u16* vg = static_cast<const u16*>(a.v) + b * a.v_sb + h * a.v_sh + kv0 * a.v_ss;
 
   // Q^T fragments for this lane's query row, kept for the whole key loop.
   const int row = qt * T::BM + wave * 32 + li;
   bf16x8 qf[T::NK];
+  {
+    const __amdgpu_buffer_rsrc_t qr =
+        rows_rsrc(qg, (int64_t)qt * T::BM, a.q_ss, a.Sq - qt * T::BM, T::BM);
+    const int qoff = ((wave * 32 + li) * (int)a.q_ss + lh * 8) * 2;
 #pragma unroll
-  for (int ks = 0; ks < T::NK; ++ks) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (row < a.Sq) x = ld16(qg + (int64_t)row * a.q_ss + ks * 16 + lh * 8);
-    qf[ks] = as_bf16x8(x);
+    for (int ks = 0; ks < T::NK; ++ks)
+      qf[ks] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(qr, qoff + ks * 32, 0, 0));
   }
 
   f32x16 oacc[T::ND];
@@ -146,131 +206,193 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
   const int nkv = kv1 - kv0;
   const int ntiles = (nkv + T::BC - 1) / T::BC;
 
-  // Global -> register staging of one K/V tile.
-  u32x4 kreg[T::KLOADS];
-  u32x4 vreg[4];
-  const int vjg = tid % T::VJG;   // V: keys 4*vjg .. 4*vjg+3
-  const int vdc = tid / T::VJG;   //    dims 8*vdc .. 8*vdc+7
-  auto gload = [&](int t) {
-    const int base = kv0 + t * T::BC;
+  // Global byte offsets of this lane's 16-byte loads (constant over tiles):
+  // load `it` of wave w fills LDS chunks (it*4 + w)*64 + lane of the tile.
+  int koff[T::NLOAD], voff[T::NLOAD];
 #pragma unroll
-    for (int it = 0; it < T::KLOADS; ++it) {
-      const int c = it * kThreads + tid;
-      const int r = c / T::KCH, col = c % T::KCH;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (base + r < kv1) x = ld16(kg + (int64_t)(base + r) * a.k_ss + col * 8);
-      kreg[it] = x;
-    }
+  for (int it = 0; it < T::NLOAD; ++it) {
+    const int P = (it * 4 + wave) * 64 + lane;
+    const int R = P / T::KCH, pc = P % T::KCH;
+    koff[it] = key_row(R) * (int)a.k_ss * 2 + (pc ^ T::kx(R)) * 16;
+    voff[it] = R * (int)a.v_ss * 2 + (pc ^ T::vx(R)) * 16;
+  }
+  // LDS byte offsets of this lane's operand reads (constant over tiles).
+  int kread[T::NK];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = base + 4 * vjg + r;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < kv1) x = ld16(vg + (int64_t)key * a.v_ss + vdc * 8);
-      vreg[r] = x;
-    }
-  };
-  auto lstore = [&](int buf) {
-    u16* ks = lds + buf * T::STAGE;
-    u16* vt = ks + T::K_LDS;
+  for (int k = 0; k < T::NK; ++k) kread[k] = li * T::RB + 16 * ((2 * k + lh) ^ T::kx(li));
+  int vread[T::ND];
+  {
+    const int g = lane >> 4, i = lane & 15;
+    const int key = 8 * (g >> 1) + (i >> 2);          // + jb*32 + hf*16 + 4u
+    const int x = 2 * (g & 1) + ((i & 3) >> 1);       // chunk within the 64-byte d block
 #pragma unroll
-    for (int it = 0; it < T::KLOADS; ++it) {
-      const int c = it * kThreads + tid;
-      const int r = c / T::KCH, col = c % T::KCH;
-      *reinterpret_cast<u32x4*>(ks + key_row(r) * T::KP + col * 8) = kreg[it];
-    }
-    // 4 keys x 8 dims -> 8 rows of V^T, 4 keys each
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      unsigned lo, hi;
-      if (e & 1) {
-        lo = (vreg[0][w] >> 16) | (vreg[1][w] & 0xffff0000u);
-        hi = (vreg[2][w] >> 16) | (vreg[3][w] & 0xffff0000u);
-      } else {
-        lo = (vreg[0][w] & 0xffffu) | (vreg[1][w] << 16);
-        hi = (vreg[2][w] & 0xffffu) | (vreg[3][w] << 16);
-      }
-      u32x2 pair = {lo, hi};
-      *reinterpret_cast<u32x2*>(vt + (vdc * 8 + e) * T::VP + 4 * vjg) = pair;
-    }
-  };
+    for (int db = 0; db < T::ND; ++db)
+      vread[db] = key * T::RB + 16 * ((4 * db + x) ^ T::vx(i >> 2)) + 8 * (i & 1);
+  }
 
-  if (ntiles > 0) gload(0);
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    lstore(buf);
-    __syncthreads();
-    if (t + 1 < ntiles) gload(t + 1);
-    const u16* ks = lds + buf * T::STAGE;
-    const u16* vt = ks + T::K_LDS;
-
-    // S^T = K Q^T for NJ blocks of 32 keys
-    f32x16 s[T::NJ];
+  auto dma = [&](char* dst, const u16* src, int64_t stride, int t, const int (&off)[T::NLOAD]) {
+    const __amdgpu_buffer_rsrc_t r = rows_rsrc(src, (int64_t)t * T::BC, stride, nkv - t * T::BC, T::BC);
 #pragma unroll
-    for (int jb = 0; jb < T::NJ; ++jb) {
+    for (int it = 0; it < T::NLOAD; ++it)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + (it * 4 + wave) * 1024), 16,
+                                               off[it], 0, 0, 0);
+  };
+  // S^T = K Q^T for the NJ 32-key blocks of the tile in kb
+  auto qk = [&](const char* kb, f32x16 (&s)[T::NJ]) {
+#pragma unroll
+    for (int jb = 0; jb < T::NJ; ++jb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[jb][r] = 0.0f;
 #pragma unroll
-      for (int k = 0; k < T::NK; ++k) {
-        const bf16x8 kf = as_bf16x8(ld16(ks + (jb * 32 + li) * T::KP + k * 16 + lh * 8));
+    for (int k = 0; k < T::NK; ++k)
+#pragma unroll
+      for (int jb = 0; jb < T::NJ; ++jb) {
+        const bf16x8 kf = as_bf16x8(lds_read16(kb, jb * 32 * T::RB + kread[k]));
         s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[k], s[jb], 0, 0, 0);
       }
-    }
-
-    // keys past the end of the range do not exist
-    const int valid = nkv - t * T::BC;
-    if (valid < T::BC) {
-#pragma unroll
-      for (int jb = 0; jb < T::NJ; ++jb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = jb * 32 + 16 * (r >> 3) + 8 * lh + (r & 7);
-          if (key >= valid) s[jb][r] = -__builtin_inff();
-        }
-    }
-
-    // online softmax: tile max of this row (both halves), lazy rescale
-    float mx = s[0][0];
-#pragma unroll
-    for (int jb = 0; jb < T::NJ; ++jb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mxs = mx * a.scale_log2;
-    if (__ballot(mxs > m + kTau) != 0ull) {
-      const float mn = fmaxf(m, mxs);
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < T::ND; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      m = mn;
-    }
-
-    // P = 2^(s*scale*log2e - m), rounded to bf16 for the P V product
-    bf16x8 pf[T::NJ][2];
-#pragma unroll
-    for (int jb = 0; jb < T::NJ; ++jb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int t8 = 0; t8 < 8; ++t8) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jb][hf * 8 + t8], a.scale_log2, -m));
-          l += p;
-          pf[jb][hf][t8] = (__bf16)p;
-        }
-
-    // O^T += V^T P^T
+  };
+  // O^T += V^T P^T for the tile in vb
+  auto pv = [&](const char* vb, const bf16x8 (&pf)[T::NJ][2]) {
 #pragma unroll
     for (int jb = 0; jb < T::NJ; ++jb)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int db = 0; db < T::ND; ++db) {
-          const bf16x8 vf = as_bf16x8(ld16(vt + (db * 32 + li) * T::VP + jb * 32 + hf * 16 + lh * 8));
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[jb][hf], oacc[db], 0, 0, 0);
+          const int kb0 = (jb * 32 + hf * 16) * T::RB;
+          // keys +0..3 and +4..7 of the 8 this lane contributes; joined as
+          // whole 64-bit words (no per-element conversion)
+          const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr(vb, kb0 + vread[db]));
+          const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr(vb, kb0 + 4 * T::RB + vread[db]));
+          const bf16x8 va = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[jb][hf], oacc[db], 0, 0, 0);
         }
+  };
+
+  // One tile t: start the loads of K (tile t+1) and V (tile t), S^T of tile
+  // t, its softmax, and the P V product of tile t-1 (whose P is p_prev).
+  // Out-of-range tiles read as zero through their descriptors, so the body
+  // has no per-tile conditions; the last tile is a separate instance that
+  // masks the keys past the end of the range.
+  auto step = [&](const char* kb_t, char* kb_n, char* vb_t, const char* vb_p,
+                  const bf16x8 (&p_prev)[T::NJ][2], bf16x8 (&p_new)[T::NJ][2], int t,
+                  auto first_tag, auto last_tag) {
+    constexpr bool kFirst = decltype(first_tag)::value;
+    constexpr bool kLastTile = decltype(last_tag)::value;
+    __syncthreads();            // tile t's K and tile t-1's V are in; kb_n, vb_t are free
+    dma(kb_n, kg, a.k_ss, t + 1, koff);
+    dma(vb_t, vg, a.v_ss, t, voff);
+
+    f32x16 sc[T::NJ];
+    qk(kb_t, sc);
+
+    if constexpr (kLastTile) {
+      // keys past the end of the range do not exist
+      const int valid = nkv - t * T::BC;
+#pragma unroll
+      for (int jb = 0; jb < T::NJ; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = jb * 32 + 16 * (r >> 3) + 8 * lh + (r & 7);
+          if (key >= valid) sc[jb][r] = -__builtin_inff();
+        }
+    }
+
+    // online softmax: tile max of this row (both halves), running max
+    float mx = sc[0][0];
+#pragma unroll
+    for (int jb = 0; jb < T::NJ; ++jb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[jb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx * a.scale_log2);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    l *= alpha;
+    m = mn;
+
+    if constexpr (!kFirst) pv(vb_p, p_prev);
+    // O through tile t-1 was relative to the old max: rescale it (alpha is
+    // exactly 1 when the max did not move, so the product is then exact)
+#pragma unroll
+    for (int db = 0; db < T::ND; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+
+    // P = 2^(s*scale*log2e - m) <= 1, summed in fp32 for l (and so for the
+    // LSE) and rounded to bf16 (nearest even) for the P V product
+#pragma unroll
+    for (int jb = 0; jb < T::NJ; ++jb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int t2 = 0; t2 < 4; ++t2) {
+          const float p0 = __builtin_amdgcn_exp2f(
+              __builtin_fmaf(sc[jb][hf * 8 + 2 * t2], a.scale_log2, -m));
+          const float p1 = __builtin_amdgcn_exp2f(
+              __builtin_fmaf(sc[jb][hf * 8 + 2 * t2 + 1], a.scale_log2, -m));
+          l += p0;
+          l += p1;
+          const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+          p_new[jb][hf][2 * t2] = pp[0];
+          p_new[jb][hf][2 * t2 + 1] = pp[1];
+        }
+
+    // Instruction order for the block above: the loads, then K reads with
+    // the QK^T MFMAs, then (after the row max) each P V MFMA of tile t-1
+    // followed by two V reads for a later one and a share of the softmax
+    // vector work, so one wave keeps both the matrix and the vector pipes fed.
+    constexpr int kQK = T::NJ * T::NK;
+    constexpr int kPV = T::NJ * 2 * T::ND;
+    __builtin_amdgcn_sched_group_barrier(0x020, 2 * T::NLOAD, 0);   // VMEM: the LDS loads
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);               // first K reads
+#pragma unroll
+    for (int i = 0; i < kQK; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // QK^T MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // next K read
+    }
+    if constexpr (!kFirst) {
+      constexpr int kValuPerMfma = (3 * T::NJ * 16 + T::NJ * 8 + T::ND * 16 + kPV - 1) / kPV;
+      __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);            // row max
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);             // first V reads
+#pragma unroll
+      for (int i = 0; i < kPV; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // P V MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);           // V reads ahead
+        __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);  // softmax VALU
+      }
+    }
+
+    // this wave's loads must land before the next barrier publishes them
+    __builtin_amdgcn_s_waitcnt(kWaitVmem);
+  };
+
+  if (ntiles > 0) {
+    dma(kbuf0, kg, a.k_ss, 0, koff);
+    __builtin_amdgcn_s_waitcnt(kWaitVmem);
+    bf16x8 pa[T::NJ][2], pb[T::NJ][2];
+    // Tiles come in (odd, even) pairs after tile 0; buffers alternate by parity.
+    if (ntiles == 1) {
+      step(kbuf0, kbuf1, vbuf0, vbuf1, pb, pa, 0, First{}, Last{});
+      __syncthreads();
+      pv(vbuf0, pa);
+    } else {
+      step(kbuf0, kbuf1, vbuf0, vbuf1, pb, pa, 0, First{}, NotLast{});
+      int t = 1;
+      for (; t + 2 < ntiles; t += 2) {
+        step(kbuf1, kbuf0, vbuf1, vbuf0, pa, pb, t, NotFirst{}, NotLast{});
+        step(kbuf0, kbuf1, vbuf0, vbuf1, pb, pa, t + 1, NotFirst{}, NotLast{});
+      }
+      if (t + 1 < ntiles) {       // two left: t odd, t+1 even and last
+        step(kbuf1, kbuf0, vbuf1, vbuf0, pa, pb, t, NotFirst{}, NotLast{});
+        step(kbuf0, kbuf1, vbuf0, vbuf1, pb, pa, t + 1, NotFirst{}, Last{});
+        __syncthreads();
+        pv(vbuf0, pa);
+      } else {                    // one left: t odd and last
+        step(kbuf1, kbuf0, vbuf1, vbuf0, pa, pb, t, NotFirst{}, Last{});
+        __syncthreads();
+        pv(vbuf1, pb);
+      }
+    }
   }
 
   // epilogue: O = O_acc / l, LSE = (m + log2 l) ln 2; no keys -> O = 0, -inf
@@ -297,6 +419,7 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
     if (lh == 0 && a.lse != nullptr)
       a.lse[split * a.l_split_stride + b * a.l_sb + h * a.l_sh + row] = lse;
   }
+#endif
 }
 
 template <int D, bool OF32>

@@ -135,6 +135,15 @@ void fill_attn_views(cru::AttnArgs& a, const cru_tensor* q, const cru_tensor* k,
   a.D = (int)q->D;
 }
 
+// The bf16 kernel addresses one 128-row tile of q, k or v through a buffer
+// descriptor with a 32-bit byte range.
+cru_status check_row_strides(const cru_tensor* q, const cru_tensor* k, const cru_tensor* v) {
+  const int64_t lim = ((int64_t)1 << 31) / (128 * 4);
+  if (q->ss >= lim || k->ss >= lim || v->ss >= lim)
+    return fail(CRU_EINVAL, "sequence stride above %lld elements", (long long)lim);
+  return CRU_OK;
+}
+
 // Checks shared by the attention entry points: q, k, v, o views, dtypes, shapes.
 cru_status check_qkvo(const cru_tensor* q, const cru_tensor* k, const cru_tensor* v,
                       const cru_tensor* o) {
@@ -154,6 +163,7 @@ cru_status check_qkvo(const cru_tensor* q, const cru_tensor* k, const cru_tensor
   if (!same_shape(v, k)) return fail(CRU_EINVAL, "v shape differs from k");
   if (!same_shape(o, q)) return fail(CRU_EINVAL, "o shape differs from q");
   CRU_TRY(check_head_dim(q, "q"));
+  CRU_TRY(check_row_strides(q, k, v));
   return CRU_OK;
 }
 

@@ -178,6 +178,24 @@ def test_constant_v_and_zero_k():
     assert err(to_f64(l), np.full(l.shape, math.log(300))) <= 1e-5
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_identity_v_gives_probabilities(D):
+    # V = identity: O[i, j] is exactly the weight key j gets in row i, so any
+    # pairing of a score with the wrong value row shows up column by column
+    # (the LSE alone cannot see it: it does not depend on the key order)
+    q, k, _ = random_qkv(15, 1, 160, D, 2, D, gain=2.0)
+    v = torch.zeros(1, D, 2, D, dtype=torch.bfloat16)
+    for j in range(D):
+        v[0, j, :, j] = 1.0
+    o, _ = cru.attn_fwd_lse(*cuda(q, k, v), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    s = np.einsum("bihd,bjhd->bhij", to_f64(q), to_f64(k)) / math.sqrt(D)
+    p = np.exp(s - s.max(-1, keepdims=True))
+    p /= p.sum(-1, keepdims=True)
+    got = np.transpose(to_f64(o), (0, 2, 1, 3))          # [b, h, i, j]
+    assert err(got, p) <= 4e-3                           # bf16 rounding of P
+
+
 # --------------------------------------------------------------------- merge
 
 @pytest.mark.parametrize("n", [1, 2, 5, 8, 13, 17, 40])
