@@ -12,7 +12,8 @@
 // memory).
 //
 // Work decomposition
-//   workgroup = 4 waves = one tile of 128 query rows of one (split, b, h);
+//   workgroup = 8 waves = one tile of 256 query rows of one (split, b, h),
+//               two waves on each of the CU's four SIMDs;
 //   wave      = 32 query rows; lane (i = lane%32, half = lane/32).
 //   Key tiles of 64 keys go from global memory straight into LDS (buffer
 //   loads with the LDS destination bit: 64 lanes write 1 KiB contiguously,
@@ -55,11 +56,14 @@
 // with no per-load bounds arithmetic.
 //
 // The running max m is kept in log2 units (scores times scale*log2(e)), so
-// P = 2^(x - m) <= 1 is one FMA and one v_exp_f32 per score.  The rescale of
-// O by 2^(m_old - m_new) is applied every tile without a branch (it is an
-// exact multiply by 1 when the max does not move), which keeps each tile's
-// instructions in one block for the scheduler.  The row sum l adds the fp32
-// P; only the P V product sees P rounded to bf16.
+// P = 2^(x - m) is one FMA and one v_exp_f32 per score.  Rescaling is lazy:
+// m only moves when some row's tile max passes it by more than kTau, so P
+// may reach 2^kTau (fp32 sums and bf16 P hold that as well as values below
+// 1) and the 64-register rescale of O is rare.  The rescale a move owes is
+// settled at the start of the next tile, ahead of its QK^T block, so its
+// branch never splits the block the compiler interleaves (QK^T, max, P V of
+// the previous tile, exponentials).  The row sum l adds the fp32 P; only the
+// P V product sees P rounded to bf16.
 #include "cru_kernels.h"
 
 namespace cru {
@@ -74,15 +78,20 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16;
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr float kTau = 8.0f;   // lazy rescale threshold, log2 units
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
 constexpr int kWaitVmem = 0x0F70;        // s_waitcnt vmcnt(0), other counters not waited
+// Half-step offset between the two wave groups that share each SIMD (see
+// "Software pipeline" above).
+constexpr bool kPingPong = false;
 
 template <int D>
 struct Tile {
   static constexpr int BC = 64;                // keys per tile
-  static constexpr int BM = 128;               // query rows per workgroup
+  static constexpr int BM = 32 * kWaves;        // query rows per workgroup
   static constexpr int RB = 2 * D;             // bytes per K or V row in LDS
   static constexpr int KCH = D / 8;            // 16-byte chunks per row
   static constexpr int NJ = BC / 32;           // 32-key blocks per tile
@@ -156,7 +165,7 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keep it scalar
   const int li = lane & 31;
   const int lh = lane >> 5;
 
@@ -202,16 +211,20 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
   float m = -__builtin_inff();   // running max of s * scale * log2(e)
   float l = 0.0f;                // this half-lane's share of the running sum
+  // Rescale of O still owed for the last max move (applied just before the
+  // next P V product, see the step below).
+  float alpha_owed = 1.0f;
+  bool owed = false;
 
   const int nkv = kv1 - kv0;
   const int ntiles = (nkv + T::BC - 1) / T::BC;
 
   // Global byte offsets of this lane's 16-byte loads (constant over tiles):
-  // load `it` of wave w fills LDS chunks (it*4 + w)*64 + lane of the tile.
+  // load `it` of wave w fills LDS chunks (it*kWaves + w)*64 + lane of the tile.
   int koff[T::NLOAD], voff[T::NLOAD];
 #pragma unroll
   for (int it = 0; it < T::NLOAD; ++it) {
-    const int P = (it * 4 + wave) * 64 + lane;
+    const int P = (it * kWaves + wave) * 64 + lane;
     const int R = P / T::KCH, pc = P % T::KCH;
     koff[it] = key_row(R) * (int)a.k_ss * 2 + (pc ^ T::kx(R)) * 16;
     voff[it] = R * (int)a.v_ss * 2 + (pc ^ T::vx(R)) * 16;
@@ -234,7 +247,7 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
     const __amdgpu_buffer_rsrc_t r = rows_rsrc(src, (int64_t)t * T::BC, stride, nkv - t * T::BC, T::BC);
 #pragma unroll
     for (int it = 0; it < T::NLOAD; ++it)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + (it * 4 + wave) * 1024), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + (it * kWaves + wave) * 1024), 16,
                                                off[it], 0, 0, 0);
   };
   // S^T = K Q^T for the NJ 32-key blocks of the tile in kb
@@ -281,7 +294,19 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
     constexpr bool kLastTile = decltype(last_tag)::value;
     __syncthreads();            // tile t's K and tile t-1's V are in; kb_n, vb_t are free
     dma(kb_n, kg, a.k_ss, t + 1, koff);
-    dma(vb_t, vg, a.v_ss, t, voff);
+    if constexpr (!kPingPong) dma(vb_t, vg, a.v_ss, t, voff);
+    // O holds tiles up to t-2 relative to the max before tile t-1's move;
+    // settle that rescale (rare: only when the max moved) before tile t-1 is
+    // added below.  Settling here, ahead of the QK^T block, keeps its branch
+    // out of the block so the compiler can interleave the whole tile.
+    if constexpr (!kFirst) {
+      if (owed) {
+#pragma unroll
+        for (int db = 0; db < T::ND; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha_owed;
+      }
+    }
 
     f32x16 sc[T::NJ];
     qk(kb_t, sc);
@@ -298,27 +323,39 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
         }
     }
 
-    // online softmax: tile max of this row (both halves), running max
+    // online softmax: tile max of this row (both halves); the running max
+    // only moves when some row's tile max passes it by more than kTau
     float mx = sc[0][0];
 #pragma unroll
     for (int jb = 0; jb < T::NJ; ++jb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[jb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(m, mx * a.scale_log2);
+    const float mxs = mx * a.scale_log2;
+    const bool move = __ballot(mxs > m + kTau) != 0ull;
+    const float mn = move ? fmaxf(m, mxs) : m;
     const float alpha = __builtin_amdgcn_exp2f(m - mn);
     l *= alpha;
     m = mn;
 
-    if constexpr (!kFirst) pv(vb_p, p_prev);
-    // O through tile t-1 was relative to the old max: rescale it (alpha is
-    // exactly 1 when the max did not move, so the product is then exact)
-#pragma unroll
-    for (int db = 0; db < T::ND; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    if constexpr (kPingPong) {
+      // half-step barrier: K of tile t+1 is published here, and V of tile t
+      // is loaded only now, after the other group's last read of tile t-2
+      __builtin_amdgcn_s_waitcnt(kWaitVmem);
+      __syncthreads();
+      dma(vb_t, vg, a.v_ss, t, voff);
+    }
 
-    // P = 2^(s*scale*log2e - m) <= 1, summed in fp32 for l (and so for the
+    if constexpr (!kFirst) {
+      // tile t-1, whose P is relative to the max after its move
+      pv(vb_p, p_prev);
+    }
+    // tiles up to t-1 are now in O relative to the max before this tile's
+    // move (tile 0 leaves O empty, so nothing is owed after it)
+    owed = kFirst ? false : move;
+    alpha_owed = alpha;
+
+    // P = 2^(s*scale*log2e - m) <= 2^kTau, summed in fp32 for l (and so for the
     // LSE) and rounded to bf16 (nearest even) for the P V product
 #pragma unroll
     for (int jb = 0; jb < T::NJ; ++jb)
@@ -337,44 +374,41 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
           p_new[jb][hf][2 * t2 + 1] = pp[1];
         }
 
-    // Instruction order for the block above: the loads, then K reads with
-    // the QK^T MFMAs, then (after the row max) each P V MFMA of tile t-1
-    // followed by two V reads for a later one and a share of the softmax
-    // vector work, so one wave keeps both the matrix and the vector pipes fed.
-    constexpr int kQK = T::NJ * T::NK;
-    constexpr int kPV = T::NJ * 2 * T::ND;
-    __builtin_amdgcn_sched_group_barrier(0x020, 2 * T::NLOAD, 0);   // VMEM: the LDS loads
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);               // first K reads
-#pragma unroll
-    for (int i = 0; i < kQK; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // QK^T MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // next K read
-    }
-    if constexpr (!kFirst) {
-      constexpr int kValuPerMfma = (3 * T::NJ * 16 + T::NJ * 8 + T::ND * 16 + kPV - 1) / kPV;
-      __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);            // row max
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);             // first V reads
-#pragma unroll
-      for (int i = 0; i < kPV; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // P V MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);           // V reads ahead
-        __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);  // softmax VALU
-      }
-    }
-
     // this wave's loads must land before the next barrier publishes them
     __builtin_amdgcn_s_waitcnt(kWaitVmem);
   };
 
+  // Before the last P V: the last tile's V is complete once both groups
+  // have passed the barrier after their own loads of it.
+  auto tail_sync = [&]() {
+    __syncthreads();
+    if constexpr (kPingPong) __syncthreads();
+  };
+
+  auto settle = [&]() {
+    if (owed) {
+#pragma unroll
+      for (int db = 0; db < T::ND; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha_owed;
+    }
+  };
+
+  // With the half-step offset the late group passes one extra barrier at
+  // the start and the early group one at the end, so both pass the same
+  // number and every barrier instance pairs step t of one group with the
+  // half-step before it of the other.
+  const bool late = kPingPong && wave >= kWaves / 2;
   if (ntiles > 0) {
     dma(kbuf0, kg, a.k_ss, 0, koff);
     __builtin_amdgcn_s_waitcnt(kWaitVmem);
+    if (late) __syncthreads();
     bf16x8 pa[T::NJ][2], pb[T::NJ][2];
     // Tiles come in (odd, even) pairs after tile 0; buffers alternate by parity.
     if (ntiles == 1) {
       step(kbuf0, kbuf1, vbuf0, vbuf1, pb, pa, 0, First{}, Last{});
-      __syncthreads();
-      pv(vbuf0, pa);
+      tail_sync();
+      pv(vbuf0, pa);            // nothing owed after tile 0
     } else {
       step(kbuf0, kbuf1, vbuf0, vbuf1, pb, pa, 0, First{}, NotLast{});
       int t = 1;
@@ -385,15 +419,19 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
       if (t + 1 < ntiles) {       // two left: t odd, t+1 even and last
         step(kbuf1, kbuf0, vbuf1, vbuf0, pa, pb, t, NotFirst{}, NotLast{});
         step(kbuf0, kbuf1, vbuf0, vbuf1, pb, pa, t + 1, NotFirst{}, Last{});
-        __syncthreads();
+        tail_sync();
+        settle();
         pv(vbuf0, pa);
       } else {                    // one left: t odd and last
         step(kbuf1, kbuf0, vbuf1, vbuf0, pa, pb, t, NotFirst{}, Last{});
-        __syncthreads();
+        tail_sync();
+        settle();
         pv(vbuf1, pb);
       }
     }
   }
+
+  if (kPingPong && ntiles > 0 && !late) __syncthreads();
 
   // epilogue: O = O_acc / l, LSE = (m + log2 l) ln 2; no keys -> O = 0, -inf
   const float lt = l + __shfl_xor(l, 32);
