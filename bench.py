@@ -5,7 +5,9 @@ attention shape (B=1, H=24, S=4096+512=4608, D=128, bf16, synthetic inputs):
 
   1. the full forward: attention with per-row LSE over all 4608 rows;
   2. ring rank 0's share at ring degree 8: its 576 query rows against the
-     8 K/V chunks, one launch per chunk in ring order, then the fold;
+     8 K/V chunks (all resident, as after the ring's all-gather), the 8
+     per-chunk partials from one split-KV launch, then the in-order fold
+     (bitwise the same result as one launch per chunk);
   3. the 8-way LSE merge over all 4608 rows (8 fp32 partials -> bf16 O);
   4. Ulysses rank 0's share at degree 2: seq2head of Q, K, V, attention over
      its 12 heads at full length, head2seq of the output.
@@ -179,7 +181,7 @@ def main():
         if m: m[0].record(stream)
         cru.attn_fwd_lse(q, k, v, out=o_full, lse=l_full)
         if m: m[1].record(stream)
-        cru.ring_emulate(q_share, k, v, N, out=o_ring, lse=l_ring, workspace=ws)
+        cru.ring_emulate(q_share, k, v, N, fused=True, out=o_ring, lse=l_ring, workspace=ws)
         if m: m[2].record(stream)
         cru.attn_merge_lse(parts_o, parts_l, out=o_merge, lse=l_merge)
         if m: m[3].record(stream)
@@ -281,7 +283,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "flux-1024", "B": B, "H": H, "S": S, "D": D,
                    "ring_degree": N, "ulysses_degree": P,
-                   "step": "full forward + ring rank-0 share (8 chunks, step-wise) + "
+                   "step": "full forward + ring rank-0 share (8 chunks, one split-KV launch) + "
                            "8-way merge over all rows + Ulysses rank-0 share (P=2)",
                    "step_attention_flops": step_flops},
         "roofline": roofline,

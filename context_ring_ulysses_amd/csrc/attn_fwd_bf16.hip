@@ -12,8 +12,9 @@
 // memory).
 //
 // Work decomposition
-//   workgroup = 8 waves = one tile of 256 query rows of one (split, b, h),
-//               two waves on each of the CU's four SIMDs;
+//   workgroup = W waves = one tile of 32*W query rows of one (split, b, h);
+//               W = 8 (two waves on each of the CU's four SIMDs) for large
+//               launches, 4 or 2 where that leaves fewer idle CUs or rows;
 //   wave      = 32 query rows; lane (i = lane%32, half = lane/32).
 //   Key tiles of 64 keys go from global memory straight into LDS (buffer
 //   loads with the LDS destination bit: 64 lanes write 1 KiB contiguously,
@@ -64,6 +65,7 @@
 // branch never splits the block the compiler interleaves (QK^T, max, P V of
 // the previous tile, exponentials).  The row sum l adds the fp32 P; only the
 // P V product sees P rounded to bf16.
+#include "attn_shape.h"
 #include "cru_kernels.h"
 
 namespace cru {
@@ -78,20 +80,17 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16;
 
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
 constexpr float kTau = 8.0f;   // lazy rescale threshold, log2 units
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
 constexpr int kWaitVmem = 0x0F70;        // s_waitcnt vmcnt(0), other counters not waited
-// Half-step offset between the two wave groups that share each SIMD (see
-// "Software pipeline" above).
-constexpr bool kPingPong = false;
 
-template <int D>
+template <int D, int W>
 struct Tile {
+  static constexpr int kWaves = W;             // waves per workgroup
+  static constexpr int kThreads = 64 * W;
   static constexpr int BC = 64;                // keys per tile
-  static constexpr int BM = 32 * kWaves;        // query rows per workgroup
+  static constexpr int BM = 32 * W;            // query rows per workgroup
   static constexpr int RB = 2 * D;             // bytes per K or V row in LDS
   static constexpr int KCH = D / 8;            // 16-byte chunks per row
   static constexpr int NJ = BC / 32;           // 32-key blocks per tile
@@ -149,15 +148,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const u16* base, int
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(p), (short)0, bytes, kRsrcWord3);
 }
 
-template <int D, bool OF32>
-__global__ void __launch_bounds__(kThreads)
+template <int D, bool OF32, int W>
+__global__ void __launch_bounds__(64 * W)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_bf16_kernel(const AttnArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   // The body is compiled for the device only; the host pass needs just the
   // signature for the launch stub (it cannot type-check the gfx950 LDS
   // builtins used below).
-  using T = Tile<D>;
+  using T = Tile<D, W>;
+  constexpr int kWaves = W;
   __shared__ __attribute__((aligned(1024))) char kbuf0[T::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char kbuf1[T::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf0[T::TILE_BYTES];
@@ -294,7 +294,7 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
     constexpr bool kLastTile = decltype(last_tag)::value;
     __syncthreads();            // tile t's K and tile t-1's V are in; kb_n, vb_t are free
     dma(kb_n, kg, a.k_ss, t + 1, koff);
-    if constexpr (!kPingPong) dma(vb_t, vg, a.v_ss, t, voff);
+    dma(vb_t, vg, a.v_ss, t, voff);
     // O holds tiles up to t-2 relative to the max before tile t-1's move;
     // settle that rescale (rare: only when the max moved) before tile t-1 is
     // added below.  Settling here, ahead of the QK^T block, keeps its branch
@@ -338,14 +338,6 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
     l *= alpha;
     m = mn;
 
-    if constexpr (kPingPong) {
-      // half-step barrier: K of tile t+1 is published here, and V of tile t
-      // is loaded only now, after the other group's last read of tile t-2
-      __builtin_amdgcn_s_waitcnt(kWaitVmem);
-      __syncthreads();
-      dma(vb_t, vg, a.v_ss, t, voff);
-    }
-
     if constexpr (!kFirst) {
       // tile t-1, whose P is relative to the max after its move
       pv(vb_p, p_prev);
@@ -378,13 +370,6 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(kWaitVmem);
   };
 
-  // Before the last P V: the last tile's V is complete once both groups
-  // have passed the barrier after their own loads of it.
-  auto tail_sync = [&]() {
-    __syncthreads();
-    if constexpr (kPingPong) __syncthreads();
-  };
-
   auto settle = [&]() {
     if (owed) {
 #pragma unroll
@@ -394,20 +379,14 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
     }
   };
 
-  // With the half-step offset the late group passes one extra barrier at
-  // the start and the early group one at the end, so both pass the same
-  // number and every barrier instance pairs step t of one group with the
-  // half-step before it of the other.
-  const bool late = kPingPong && wave >= kWaves / 2;
   if (ntiles > 0) {
     dma(kbuf0, kg, a.k_ss, 0, koff);
     __builtin_amdgcn_s_waitcnt(kWaitVmem);
-    if (late) __syncthreads();
     bf16x8 pa[T::NJ][2], pb[T::NJ][2];
     // Tiles come in (odd, even) pairs after tile 0; buffers alternate by parity.
     if (ntiles == 1) {
       step(kbuf0, kbuf1, vbuf0, vbuf1, pb, pa, 0, First{}, Last{});
-      tail_sync();
+      __syncthreads();
       pv(vbuf0, pa);            // nothing owed after tile 0
     } else {
       step(kbuf0, kbuf1, vbuf0, vbuf1, pb, pa, 0, First{}, NotLast{});
@@ -419,19 +398,17 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
       if (t + 1 < ntiles) {       // two left: t odd, t+1 even and last
         step(kbuf1, kbuf0, vbuf1, vbuf0, pa, pb, t, NotFirst{}, NotLast{});
         step(kbuf0, kbuf1, vbuf0, vbuf1, pb, pa, t + 1, NotFirst{}, Last{});
-        tail_sync();
+        __syncthreads();
         settle();
         pv(vbuf0, pa);
       } else {                    // one left: t odd and last
         step(kbuf1, kbuf0, vbuf1, vbuf0, pa, pb, t, NotFirst{}, Last{});
-        tail_sync();
+        __syncthreads();
         settle();
         pv(vbuf1, pb);
       }
     }
   }
-
-  if (kPingPong && ntiles > 0 && !late) __syncthreads();
 
   // epilogue: O = O_acc / l, LSE = (m + log2 l) ln 2; no keys -> O = 0, -inf
   const float lt = l + __shfl_xor(l, 32);
@@ -460,15 +437,37 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
 #endif
 }
 
-template <int D, bool OF32>
-hipError_t launch(const AttnArgs& a, hipStream_t stream) {
-  using T = Tile<D>;
+template <int D, bool OF32, int W>
+hipError_t launch_w(const AttnArgs& a, hipStream_t stream) {
+  using T = Tile<D, W>;
   const int nqt = (a.Sq + T::BM - 1) / T::BM;
   const long total = (long)a.n_split * a.B * a.H * nqt;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OF32>), dim3((unsigned)total), dim3(kThreads), 0,
-                     stream, a);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, OF32, W>), dim3((unsigned)total),
+                     dim3(T::kThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+int cu_count() {
+  static int n = 0;   // the same for every MI355X; read once
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+template <int D, bool OF32>
+hipError_t launch(const AttnArgs& a, hipStream_t stream) {
+  switch (attn_pick_waves((long)a.n_split * a.B * a.H, a.Sq, cu_count())) {
+    case 8: return launch_w<D, OF32, 8>(a, stream);
+    case 4: return launch_w<D, OF32, 4>(a, stream);
+    default: return launch_w<D, OF32, 2>(a, stream);
+  }
 }
 
 }  // namespace

@@ -135,8 +135,9 @@ void fill_attn_views(cru::AttnArgs& a, const cru_tensor* q, const cru_tensor* k,
   a.D = (int)q->D;
 }
 
-// The bf16 kernel addresses one 128-row tile of q, k or v through a buffer
-// descriptor with a 32-bit byte range.
+// The bf16 kernel addresses one tile of q (at most 256 rows of 2-byte
+// elements) or of k, v (64 rows) through a buffer descriptor with a 32-bit
+// byte range: 256 * ss * 2 must stay below 2^31.
 cru_status check_row_strides(const cru_tensor* q, const cru_tensor* k, const cru_tensor* v) {
   const int64_t lim = ((int64_t)1 << 31) / (128 * 4);
   if (q->ss >= lim || k->ss >= lim || v->ss >= lim)
@@ -179,9 +180,11 @@ cru_status check_index_range(int64_t count, const char* what) {
   return CRU_OK;
 }
 
-// Workgroups of the attention kernels: (splits x B x H x query tiles of 128 rows).
+// Threads of the attention kernels: (splits x B x H x query tiles), two
+// threads per query row of a tile (32 rows per wave of 64 lanes); the tile
+// height is at most 256 rows.
 cru_status check_attn_grid(int64_t n_split, const cru_tensor* q) {
-  return check_index_range(n_split * q->B * q->H * ((q->S + 127) / 128) * 256, "attention");
+  return check_index_range(n_split * q->B * q->H * ((q->S + 255) / 256) * 512, "attention");
 }
 
 // Threads of the merge kernel: one per 4 elements of every row.

@@ -59,7 +59,7 @@ def inputs(idx):
 
 def sample_rows(S, n=48, seed=0):
     rng = np.random.default_rng(seed)
-    fixed = [0, 1, 63, 64, 127, 128, 129, S // 2, S - 2, S - 1]
+    fixed = [0, 1, 31, 32, 63, 64, 127, 128, 129, 255, 256, 257, S // 2, S - 2, S - 1]
     rows = set(r for r in fixed if 0 <= r < S)
     rows |= set(rng.choice(S, size=min(n, S), replace=False).tolist())
     return np.array(sorted(rows))
@@ -114,6 +114,25 @@ def test_bf16_ragged_full(D, out_dtype):
     eo, el = err(to_f64(o), o_ref), err(to_f64(l), l_ref)
     say(f"  max|dO| = {eo:.3e}, max|dLSE| = {el:.3e}")
     assert eo <= TOL_O and el <= TOL_LSE
+
+
+# The launch picks 8-, 4- or 2-wave workgroups (256, 128 or 64 query rows)
+# by how many tiles the call has; on a 256-CU MI355X these head counts give
+# each of the three shapes at Sq=300 (test_attn_shape.py checks the choice).
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("H,waves", [(128, 8), (150, 4), (8, 2)])
+def test_bf16_workgroup_shapes(H, waves, D, out_dtype):
+    q, k, v = random_qkv(300 + H + D, B=1, Sq=300, Skv=203, H=H, D=D, gain=math.sqrt(3.0))
+    say(f"bf16 H={H} (expect {waves}-wave workgroups) D={D} out={out_dtype}")
+    o, l = cru.attn_fwd_lse(*cuda(q, k, v), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
+    heads = sorted({0, 1, H // 2, H - 1})
+    rows = sample_rows(300)
+    for h in heads:
+        check_rows(o[:, :, h:h + 1], l[:, h:h + 1], q64[:, :, h:h + 1], k64[:, :, h:h + 1],
+                   v64[:, :, h:h + 1], rows, TOL_O, TOL_LSE, f"head {h}")
 
 
 @pytest.mark.parametrize("shape", [(1, 10, 10, 8, 64), (1, 1, 1, 1, 128), (3, 1, 700, 2, 64),
