@@ -252,14 +252,23 @@ def main():
     tbytes = qv.numel() * qv.element_size()
     med1, mn1 = cold(lambda: cru.ulysses_seq2head([qv, kv_, vv], Pv, out=ysv), args.cold_reps)
     med2, mn2 = cold(lambda: cru.ulysses_head2seq(ysv[0], Pv, out=ov), args.cold_reps)
+    # reference: torch's plain contiguous device copy of the same byte counts
+    # (what a copy of this size reaches on this GPU, launch and ramp included)
+    src3 = torch.empty(3 * qv.numel(), dtype=qv.dtype, device=dev)
+    dst3 = torch.empty_like(src3)
+    medc1, _ = cold(lambda: dst3.copy_(src3), args.cold_reps)
+    medc2, _ = cold(lambda: ov.copy_(qv), args.cold_reps)
+    del src3, dst3
     cold_layout = {
         "workload": "video-dit-4276 (B=2, S=4276, H=30, D=64, bf16), P=2",
         "seq2head_qkv": {"bytes": 6 * tbytes, "ms_median": med1, "ms_min": mn1,
                          "GB/s": 6 * tbytes / (med1 * 1e-3) / 1e9,
-                         "frac_hbm_peak": 6 * tbytes / (med1 * 1e-3) / 1e9 / PEAK_HBM_GBS},
+                         "frac_hbm_peak": 6 * tbytes / (med1 * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "plain_copy_same_bytes_GB/s": 6 * tbytes / (medc1 * 1e-3) / 1e9},
         "head2seq_o": {"bytes": 2 * tbytes, "ms_median": med2, "ms_min": mn2,
                        "GB/s": 2 * tbytes / (med2 * 1e-3) / 1e9,
-                       "frac_hbm_peak": 2 * tbytes / (med2 * 1e-3) / 1e9 / PEAK_HBM_GBS}}
+                       "frac_hbm_peak": 2 * tbytes / (med2 * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                       "plain_copy_same_bytes_GB/s": 2 * tbytes / (medc2 * 1e-3) / 1e9}}
     del qv, kv_, vv, ysv, ov, scrub, sink
     torch.cuda.synchronize()
 

@@ -61,7 +61,7 @@ struct LayoutArgs {
   int n;
   int elem_bytes;             // 2 or 4
   int dir;
-  FastDiv div_h, div_s, div_hp;   // set by launch_layout
+  FastDiv div_h, div_s, div_hp, div_b;   // set by launch_layout
 };
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);

@@ -10,12 +10,15 @@
 // order.  Parts with LSE_c = -inf hold no keys (w_c = 0, their O_c unused).
 //
 // Memory-bound: each part's O row is read once, O and LSE written once.
-// One thread owns VPT float4 groups of one row.  Rows are ordered (b, h, s)
-// with s fastest, so the LSE reads and writes of a wave are contiguous and
-// every O row is read as whole 16-byte vectors.  All of a thread's loads are
-// issued before the first use: the part loop is unrolled over a compile-time
-// bound with wave-uniform predicates, so nothing waits on an earlier load
-// to decide whether to issue the next.
+// One thread owns VPT float4 groups of one row.  Rows are ordered (b, s, h)
+// with h fastest, the order of [B, S, H, D] memory, so a workgroup reads one
+// contiguous run of every part (the few strided LSE reads are cache-resident
+// and reused by neighbouring workgroups).  All of a thread's loads are
+// issued before the first use: the part loop is unrolled over a
+// compile-time bound with wave-uniform predicates, so nothing waits on an
+// earlier load to decide whether to issue the next.  Loads are ordinary
+// (cached) loads and the output stores are nontemporal: on MI355X that pair
+// measured fastest for this many-stream read, one-stream write pattern.
 #include "cru_kernels.h"
 
 namespace cru {
@@ -43,10 +46,10 @@ __device__ __forceinline__ RowPos row_pos(const MergeArgs& a) {
   RowPos p;
   p.g = (int)(gid - row * gpr);
   p.live = row < (uint32_t)a.B * a.H * a.S;
-  const uint32_t bh = fdiv(row, a.div_s);
-  p.s = (int)(row - bh * a.S);
-  p.b = (int)fdiv(bh, a.div_h);
-  p.h = (int)(bh - p.b * a.H);
+  const uint32_t bs = fdiv(row, a.div_h);
+  p.h = (int)(row - bs * a.H);
+  p.b = (int)fdiv(bs, a.div_s);
+  p.s = (int)(bs - p.b * a.S);
   return p;
 }
 
@@ -58,11 +61,11 @@ __device__ __forceinline__ void store_row(const MergeArgs& a, const RowPos& p,
   for (int u = 0; u < VPT; ++u) {
     if constexpr (OF32) {
       f32x4 y = {acc[u][0] * inv, acc[u][1] * inv, acc[u][2] * inv, acc[u][3] * inv};
-      *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + odst + 4 * u) = y;
+      __builtin_nontemporal_store(y, reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + odst + 4 * u));
     } else {
       bf16x4 y = {(__bf16)(acc[u][0] * inv), (__bf16)(acc[u][1] * inv),
                   (__bf16)(acc[u][2] * inv), (__bf16)(acc[u][3] * inv)};
-      *reinterpret_cast<bf16x4*>(static_cast<u16*>(a.o) + odst + 4 * u) = y;
+      __builtin_nontemporal_store(y, reinterpret_cast<bf16x4*>(static_cast<u16*>(a.o) + odst + 4 * u));
     }
   }
   if (p.g == 0 && a.lse != nullptr) a.lse[p.b * a.l_sb + p.h * a.l_sh + p.s] = lse;
@@ -80,13 +83,12 @@ __global__ void __launch_bounds__(kThreads) merge_small(const MergeArgs a) {
   f32x4 x[NMAX][VPT];
 #pragma unroll
   for (int c = 0; c < NMAX; ++c)
-    l[c] = c < a.n ? __builtin_nontemporal_load(a.l_part[c] + loff) : -__builtin_inff();
+    l[c] = c < a.n ? a.l_part[c][loff] : -__builtin_inff();
 #pragma unroll
   for (int c = 0; c < NMAX; ++c)
 #pragma unroll
     for (int u = 0; u < VPT; ++u)
-      x[c][u] = c < a.n ? __builtin_nontemporal_load(
-                              reinterpret_cast<const f32x4*>(a.o_part[c] + ooff) + u)
+      x[c][u] = c < a.n ? reinterpret_cast<const f32x4*>(a.o_part[c] + ooff)[u]
                         : f32x4{0.f, 0.f, 0.f, 0.f};
 
   float M = l[0];
@@ -141,7 +143,7 @@ __global__ void __launch_bounds__(kThreads) merge_many(const MergeArgs a) {
       for (int u = 0; u < kBatch; ++u) {
         const bool in = c0 + u < a.n;
         l[u] = in ? a.l_part[c0 + u][loff] : -__builtin_inff();
-        x[u] = in ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.o_part[c0 + u] + ooff))
+        x[u] = in ? *reinterpret_cast<const f32x4*>(a.o_part[c0 + u] + ooff)
                   : f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll

@@ -8,11 +8,13 @@
 // The [B, S, H, D] side may be strided (d contiguous); the [P, B, S, Hp, D]
 // side is contiguous.  Pure bit-exact copies, moved 16 bytes at a time.
 //
-// Memory-bound.  Vectors are numbered in [B, S, H, D] order, so a wave reads
-// (or writes) whole (token, head) rows of the strided side, and the Hp rows
-// of one group that follow each other are one contiguous run on the packed
-// side.  The index decomposition uses multiply-high division by the
-// invariant H, S and Hp; a thread issues all its loads before its stores.
+// Memory-bound.  Vectors are numbered in the order of the source: [B, S, H,
+// D] for seq2head, [P, B, S, Hp, D] for head2seq, so the reads of a
+// workgroup are one contiguous run and the writes land in runs of Hp whole
+// rows (Hp*D elements) on the other side.  The index decomposition uses
+// multiply-high division by the invariant H, S, Hp and B; a thread issues
+// all its loads before its stores.  Plain (cached) loads and stores: on
+// MI355X they measured faster here than the nontemporal forms.
 #include "cru_kernels.h"
 
 namespace cru {
@@ -39,12 +41,23 @@ __global__ void __launch_bounds__(kThreads) layout_kernel(const LayoutArgs a) {
     const uint32_t g = base + i * kThreads;
     const uint32_t row = g / VPR;
     const int dv = (int)(g % VPR);
-    const uint32_t tok = fdiv(row, a.div_h);
-    const int h = (int)(row - tok * a.H);
-    const int b = (int)fdiv(tok, a.div_s);
-    const int s = (int)(tok - (uint32_t)b * a.S);
-    const int p = (int)fdiv((uint32_t)h, a.div_hp);
-    const int j = h - p * Hp;
+    int b, s, h, p, j;
+    if (a.dir == 0) {             // row = (b, s, h)
+      const uint32_t tok = fdiv(row, a.div_h);
+      h = (int)(row - tok * a.H);
+      b = (int)fdiv(tok, a.div_s);
+      s = (int)(tok - (uint32_t)b * a.S);
+      p = (int)fdiv((uint32_t)h, a.div_hp);
+      j = h - p * Hp;
+    } else {                      // row = (p, b, s, j)
+      const uint32_t r1 = fdiv(row, a.div_hp);
+      j = (int)(row - r1 * Hp);
+      const uint32_t r2 = fdiv(r1, a.div_s);
+      s = (int)(r1 - r2 * a.S);
+      p = (int)fdiv(r2, a.div_b);
+      b = (int)(r2 - (uint32_t)p * a.B);
+      h = p * Hp + j;
+    }
     const int64_t strided = ((int64_t)b * a.sb + (int64_t)s * a.ss + (int64_t)h * a.sh +
                              (int64_t)dv * vec_elems) * a.elem_bytes;
     const int64_t packed = (((((int64_t)p * a.B + b) * a.S + s) * Hp + j) * a.D +
@@ -52,12 +65,12 @@ __global__ void __launch_bounds__(kThreads) layout_kernel(const LayoutArgs a) {
     const int64_t from = a.dir == 0 ? strided : packed;
     to[i] = a.dir == 0 ? packed : strided;
     v[i] = u32x4{0u, 0u, 0u, 0u};
-    if (g < total) v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + from));
+    if (g < total) v[i] = *reinterpret_cast<const u32x4*>(src + from);
   }
 #pragma unroll
   for (int i = 0; i < kNV; ++i)
     if (base + i * kThreads < total)
-      __builtin_nontemporal_store(v[i], reinterpret_cast<u32x4*>(dst + to[i]));
+      *reinterpret_cast<u32x4*>(dst + to[i]) = v[i];
 }
 
 template <int VPR>
@@ -76,6 +89,7 @@ hipError_t launch_layout(const LayoutArgs& args, hipStream_t stream) {
   a.div_h = make_fastdiv((uint32_t)a.H);
   a.div_s = make_fastdiv((uint32_t)a.S);
   a.div_hp = make_fastdiv((uint32_t)(a.H / a.P));
+  a.div_b = make_fastdiv((uint32_t)a.B);
   const int vpr = a.D * a.elem_bytes / 16;
   switch (vpr) {
     case 8: return launch_vpr<8>(a, stream);
