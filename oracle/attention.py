@@ -19,7 +19,12 @@ with numpy float64 arrays.  Tensors are [B, S, H, D]; the per-row log-sum-exp
   of them; "Ring Anything Attention" section: blocks of unequal length.
 * same guide, "Ulysses Attention" section: an all-to-all regroups the data so
   a device holds every token of a subset of heads, and a second one regroups
-  the results by token.
+  the results by token; "Ulysses Anything Attention" section: the head count
+  and sequence length need not divide by the degree.
+* same guide, "Unified Attention" section: on a 2-D mesh of ulysses_degree x
+  ring_degree devices, the Ulysses all-to-all regroups heads and tokens, ring
+  attention runs on the result, and the reverse all-to-all restores the
+  layout.
 
 Readings where the pages are silent (each is also listed in the design
 notes): the softmax scale is 1/sqrt(D); LSE is the natural log; uneven
@@ -36,7 +41,8 @@ import numpy as np
 
 __all__ = ["attention", "chunk_bounds", "merge_closed_form", "merge_fold",
            "chunked_attention", "ring_share", "seq2head", "head2seq",
-           "ulysses_share"]
+           "ulysses_share", "head_groups", "groups_to_seq", "ulysses_anything_share",
+           "usp_share", "usp_attention"]
 
 NEG_INF = -np.inf
 
@@ -246,3 +252,60 @@ def ulysses_share(q, k, v, P: int, p: int, scale: Optional[float] = None
     """One Ulysses rank's share: attention over heads group p at full length."""
     qs, ks, vs = (seq2head(a, P)[p] for a in (q, k, v))
     return attention(qs, ks, vs, scale=scale)
+
+
+def head_groups(x: np.ndarray, P: int) -> List[np.ndarray]:
+    """Ulysses Anything's first all-to-all, on one device: the heads cut into
+    P consecutive groups by the near-equal rule of ``chunk_bounds`` (the first
+    H mod P groups hold one head more; groups may be empty when P > H); group
+    p is [B, S, Hp_p, D] with every token.  For H divisible by P the groups
+    are those of ``seq2head``."""
+    x = np.asarray(x)
+    _check4("x", x)
+    return [np.ascontiguousarray(x[:, :, a:b]) for a, b in chunk_bounds(x.shape[2], P)]
+
+
+def groups_to_seq(groups: Sequence[np.ndarray]) -> np.ndarray:
+    """The inverse of ``head_groups``: the groups' heads back in order."""
+    return np.ascontiguousarray(np.concatenate(list(groups), axis=2))
+
+
+def ulysses_anything_share(q, k, v, P: int, p: int, scale: Optional[float] = None
+                           ) -> Tuple[np.ndarray, np.ndarray]:
+    """One Ulysses Anything rank's share: attention over head group p."""
+    qs, ks, vs = (head_groups(a, P)[p] for a in (q, k, v))
+    return attention(qs, ks, vs, scale=scale)
+
+
+def usp_share(q, k, v, ulysses_degree: int, ring_degree: int, ulysses_rank: int,
+              ring_rank: int, scale: Optional[float] = None, merge: str = "fold"
+              ) -> Tuple[np.ndarray, np.ndarray]:
+    """The share of device (u, r) of Unified attention on a ulysses_degree x
+    ring_degree mesh: after the Ulysses regrouping it holds head group u of
+    every token, and the ring over ring_degree sequence chunks gives it the
+    query rows of chunk r.  The sequence is sharded over the whole mesh, so
+    S must divide by ulysses_degree * ring_degree."""
+    q = np.asarray(q, dtype=np.float64)
+    S = q.shape[1]
+    if S % (ulysses_degree * ring_degree):
+        raise ValueError(f"S={S} not divisible by {ulysses_degree} x {ring_degree}")
+    qs, ks, vs = (seq2head(a, ulysses_degree)[ulysses_rank] for a in (q, k, v))
+    return ring_share(qs, ks, vs, ring_degree, ring_rank, scale=scale, merge=merge)
+
+
+def usp_attention(q, k, v, ulysses_degree: int, ring_degree: int,
+                  scale: Optional[float] = None, merge: str = "fold"
+                  ) -> Tuple[np.ndarray, np.ndarray]:
+    """Every device's Unified-attention share, put back in place by the
+    reverse all-to-all: the [B, S, H, D] output and the [B, H, S] LSE."""
+    q = np.asarray(q, dtype=np.float64)
+    B, S, H, D = q.shape
+    Hp = H // ulysses_degree
+    o_groups = np.zeros((ulysses_degree, B, S, Hp, D))
+    lse = np.full((B, H, S), NEG_INF)
+    for u in range(ulysses_degree):
+        for r, (a, b) in enumerate(chunk_bounds(S, ring_degree)):
+            o, l = usp_share(q, k, v, ulysses_degree, ring_degree, u, r, scale, merge)
+            o_groups[u, :, a:b] = o
+            lse[:, u * Hp:(u + 1) * Hp, a:b] = l
+    return head2seq(o_groups, ulysses_degree), lse

@@ -335,3 +335,78 @@ def pin_ulysses_share(attn: Callable, s2h: Callable):
             os_, ls = attn(qs, ks, vs)
             _close(os_, o[:, :, p * Hp:(p + 1) * Hp], 1e-14, f"ulysses share O P={P}")
             _close(ls, lse[:, p * Hp:(p + 1) * Hp], 1e-14, f"ulysses share LSE P={P}")
+
+
+def pin_head_groups(groups: Callable, to_seq: Callable, s2h: Callable):
+    """Near-equal head groups: sizes worked out by hand, every index checked
+    by a loop, a bit-exact round trip, and the seq2head groups when P | H."""
+    rng = np.random.default_rng(21)
+    # 30 heads over 4 groups: 30 = 4*7 + 2, so the first two groups hold 8;
+    # 3 heads over 5 groups: one head each for three, two empty groups
+    for (H, P, sizes) in [(30, 4, [8, 8, 7, 7]), (3, 5, [1, 1, 1, 0, 0]), (7, 3, [3, 2, 2]),
+                          (6, 3, [2, 2, 2]), (5, 1, [5])]:
+        B, S, D = 2, 3, 2
+        x = rng.standard_normal((B, S, H, D))
+        gs = groups(x, P)
+        assert [g.shape[2] for g in gs] == sizes, f"group sizes H={H} P={P}"
+        h0 = 0
+        for g in gs:
+            assert g.shape[:2] == (B, S) and g.shape[3] == D
+            for b in range(B):
+                for s in range(S):
+                    for j in range(g.shape[2]):
+                        for d in range(D):
+                            assert g[b, s, j, d] == x[b, s, h0 + j, d], "head group index map"
+            h0 += g.shape[2]
+        back = to_seq(gs)
+        assert back.shape == x.shape and (back.view(np.uint64) == x.view(np.uint64)).all(), \
+            "group round trip not bit-exact"
+        if H % P == 0:
+            y = s2h(x, P)
+            for p in range(P):
+                assert (y[p] == gs[p]).all(), "groups differ from seq2head for P | H"
+
+
+def pin_ulysses_anything_share(attn: Callable, groups: Callable):
+    """Attention per head does not depend on the other heads, so group p's
+    share is its heads of the full result, whatever the group sizes."""
+    rng = np.random.default_rng(22)
+    q, k, v = (_rand(rng, 2, 11, 7, 8) for _ in range(3))
+    o, lse = attn(q, k, v)
+    for P in (2, 3, 4, 5):
+        h0 = 0
+        for p in range(P):
+            qs, ks, vs = (groups(a, P)[p] for a in (q, k, v))
+            hp = qs.shape[2]
+            os_, ls = attn(qs, ks, vs)
+            _close(os_, o[:, :, h0:h0 + hp], 1e-14, f"ulysses anything share O P={P}")
+            _close(ls, lse[:, h0:h0 + hp], 1e-14, f"ulysses anything share LSE P={P}")
+            h0 += hp
+        assert h0 == 7
+
+
+def pin_usp(attn: Callable, usp_attention: Callable, usp_share: Callable):
+    """Unified attention reaches the plain result: the full composition
+    equals attention to fp64 rounding, and device (u, r)'s share is rows of
+    chunk r and heads of group u of it."""
+    rng = np.random.default_rng(23)
+    B, S, H, D = 2, 24, 6, 8
+    q, k, v = (_rand(rng, B, S, H, D, s=1.5) for _ in range(3))
+    o, lse = attn(q, k, v)
+    for (Pu, Pr) in [(1, 1), (2, 2), (3, 2), (2, 4), (6, 4), (1, 3)]:
+        ou, lu = usp_attention(q, k, v, Pu, Pr)
+        _close(ou, o, 1e-12, f"usp O {Pu}x{Pr}")
+        _close(lu, lse, 1e-12, f"usp LSE {Pu}x{Pr}")
+    Pu, Pr = 3, 4
+    Hp, n = H // Pu, S // Pr
+    for u in range(Pu):
+        for r in range(Pr):
+            os_, ls = usp_share(q, k, v, Pu, Pr, u, r)
+            _close(os_, o[:, r * n:(r + 1) * n, u * Hp:(u + 1) * Hp], 1e-12, "usp share O")
+            _close(ls, lse[:, u * Hp:(u + 1) * Hp, r * n:(r + 1) * n], 1e-12, "usp share LSE")
+    try:
+        usp_share(q, k, v, 2, 5, 0, 0)          # 24 rows do not shard over 10 devices
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("usp share accepted S not divisible by the mesh")

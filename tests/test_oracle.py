@@ -43,6 +43,24 @@ def test_ulysses_share():
     pins.pin_ulysses_share(oracle.attention, oracle.seq2head)
 
 
+def test_head_groups():
+    pins.pin_head_groups(oracle.head_groups, oracle.groups_to_seq, oracle.seq2head)
+
+
+def test_ulysses_anything_share():
+    pins.pin_ulysses_anything_share(oracle.attention, oracle.head_groups)
+    # the named share function is the group of that split
+    rng = np.random.default_rng(5)
+    q, k, v = (rng.standard_normal((1, 9, 5, 4)) for _ in range(3))
+    o, l = oracle.ulysses_anything_share(q, k, v, 2, 1)
+    o_ref, l_ref = oracle.attention(q[:, :, 3:], k[:, :, 3:], v[:, :, 3:])
+    assert np.abs(o - o_ref).max() == 0 and np.abs(l - l_ref).max() == 0
+
+
+def test_usp():
+    pins.pin_usp(oracle.attention, oracle.usp_attention, oracle.usp_share)
+
+
 def test_fold_equals_closed_form_at_workload_splits():
     """The in-order fold and the one-step merge agree on real chunk partials of
     the ring-anything workload's split (S = 4645, 8 uneven chunks), and both

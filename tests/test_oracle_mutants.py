@@ -8,6 +8,7 @@ least one pin fails on the mutant, which shows the pins constrain that line.
 import importlib
 import types
 
+import numpy as np
 import pytest
 
 import pins
@@ -58,6 +59,16 @@ MUTANTS = [
     ("seq2head: heads split the wrong way", "x.reshape(B, S, P, H // P, D).transpose(2, 0, 1, 3, 4)",
      "x.reshape(B, S, H // P, P, D).transpose(3, 0, 1, 2, 4)"),
     ("head2seq: wrong inverse", "y.transpose(1, 2, 0, 3, 4)", "y.transpose(1, 2, 3, 0, 4)"),
+    ("groups: one head too many", "x[:, :, a:b]) for a, b in chunk_bounds(x.shape[2], P)]",
+     "x[:, :, a:b + 1]) for a, b in chunk_bounds(x.shape[2], P)]"),
+    ("groups: inverse reverses the order", "np.concatenate(list(groups), axis=2)",
+     "np.concatenate(list(groups)[::-1], axis=2)"),
+    ("anything share: wrong group", "(head_groups(a, P)[p] for a in (q, k, v))",
+     "(head_groups(a, P)[0] for a in (q, k, v))"),
+    ("usp: wrong ring chunk", "return ring_share(qs, ks, vs, ring_degree, ring_rank, scale=scale, merge=merge)",
+     "return ring_share(qs, ks, vs, ring_degree, 0, scale=scale, merge=merge)"),
+    ("usp: output into the wrong group", "o_groups[u, :, a:b] = o", "o_groups[0, :, a:b] = o"),
+    ("usp: LSE heads not offset", "lse[:, u * Hp:(u + 1) * Hp, a:b] = l", "lse[:, 0:Hp, a:b] = l"),
 ]
 
 
@@ -76,7 +87,20 @@ def _all_pins(m):
     checks.append(lambda: pins.pin_chunk_bounds(m.chunk_bounds))
     checks.append(lambda: pins.pin_layout(m.seq2head, m.head2seq))
     checks.append(lambda: pins.pin_ulysses_share(m.attention, m.seq2head))
+    checks.append(lambda: pins.pin_head_groups(m.head_groups, m.groups_to_seq, m.seq2head))
+    checks.append(lambda: pins.pin_ulysses_anything_share(m.attention, m.head_groups))
+    checks.append(lambda: pins.pin_usp(m.attention, m.usp_attention, m.usp_share))
+    checks.append(lambda: _anything_share_check(m))
     return checks
+
+
+def _anything_share_check(m):
+    # the named share function against the groups' own attention
+    rng = np.random.default_rng(5)
+    q, k, v = (rng.standard_normal((1, 9, 5, 4)) for _ in range(3))
+    o, l = m.ulysses_anything_share(q, k, v, 2, 1)
+    o_ref, l_ref = m.attention(q[:, :, 3:], k[:, :, 3:], v[:, :, 3:])
+    assert np.abs(o - o_ref).max() == 0 and np.abs(l - l_ref).max() == 0
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
