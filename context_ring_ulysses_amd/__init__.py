@@ -10,7 +10,9 @@ built.
 
 Entry points (same names as the C ABI without the ``cru_`` prefix):
     attn_fwd_lse, attn_merge_lse, ring_chunk_bounds, ring_workspace_bytes,
-    ring_emulate, ulysses_seq2head, ulysses_head2seq
+    ring_emulate, ulysses_head_bounds, ulysses_seq2head, ulysses_head2seq,
+    usp_workspace_bytes, usp_emulate
+plus ulysses_groups (views of the head groups of a packed buffer).
 """
 from __future__ import annotations
 
@@ -23,7 +25,8 @@ import torch
 
 __all__ = [
     "attn_fwd_lse", "attn_merge_lse", "ring_chunk_bounds", "ring_workspace_bytes",
-    "ring_emulate", "ulysses_seq2head", "ulysses_head2seq", "ContextParallelConfig",
+    "ring_emulate", "ulysses_head_bounds", "ulysses_seq2head", "ulysses_head2seq",
+    "ulysses_groups", "usp_workspace_bytes", "usp_emulate", "ContextParallelConfig",
     "lib", "LIB_PATH", "CruError", "CruInvalid", "CruNotDivisible", "CruUnsupported",
     "CruDeviceError", "CruWorkspaceError", "CruHipError", "MAX_PARTS",
 ]
@@ -112,10 +115,18 @@ def lib() -> ctypes.CDLL:
     L.cru_ring_emulate.argtypes = [T, T, T, ctypes.c_int, ctypes.c_int, _P(ctypes.c_int64),
                                    ctypes.c_int, T, Lse, ctypes.c_float, vp, ctypes.c_size_t, vp]
     L.cru_ring_emulate.restype = st
-    L.cru_ulysses_seq2head.argtypes = [ctypes.c_int, T, _P(vp), ctypes.c_int, vp]
+    L.cru_ulysses_head_bounds.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                          _P(ctypes.c_int64)]
+    L.cru_ulysses_head_bounds.restype = st
+    L.cru_ulysses_seq2head.argtypes = [ctypes.c_int, T, _P(vp), ctypes.c_int, ctypes.c_int, vp]
     L.cru_ulysses_seq2head.restype = st
-    L.cru_ulysses_head2seq.argtypes = [ctypes.c_int, _P(vp), T, ctypes.c_int, vp]
+    L.cru_ulysses_head2seq.argtypes = [ctypes.c_int, _P(vp), T, ctypes.c_int, ctypes.c_int, vp]
     L.cru_ulysses_head2seq.restype = st
+    L.cru_usp_workspace_bytes.argtypes = [T, ctypes.c_int, ctypes.c_int, _P(ctypes.c_size_t)]
+    L.cru_usp_workspace_bytes.restype = st
+    L.cru_usp_emulate.argtypes = [T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, T, Lse,
+                                  ctypes.c_float, vp, ctypes.c_size_t, vp]
+    L.cru_usp_emulate.restype = st
     L.cru_status_str.argtypes = [ctypes.c_int]
     L.cru_status_str.restype = ctypes.c_char_p
     L.cru_last_error.argtypes = []
@@ -266,60 +277,142 @@ def _as_list(x) -> Tuple[List[torch.Tensor], bool]:
     return list(x), False
 
 
+def ulysses_head_bounds(H: int, P: int, anything: bool = False) -> List[Tuple[int, int]]:
+    """Heads of each Ulysses group, [(start, end)] for p = 0..P-1 (the first
+    H mod P groups hold one head more)."""
+    starts = (ctypes.c_int64 * (max(P, 0) + 1))()
+    _check(lib().cru_ulysses_head_bounds(H, P, int(bool(anything)), starts))
+    return [(starts[p], starts[p + 1]) for p in range(P)]
+
+
+def ulysses_groups(packed: torch.Tensor, B: int, S: int, H: int, D: int, P: int
+                   ) -> List[torch.Tensor]:
+    """The [B, S, Hp_p, D] views of the head groups in a packed buffer (as
+    ulysses_seq2head writes it): group p starts at element B*S*D*h0_p."""
+    flat = packed.reshape(-1)
+    views = []
+    for (h0, h1) in ulysses_head_bounds(H, P, anything=True):
+        n = B * S * (h1 - h0) * D
+        start = B * S * D * h0
+        views.append(flat[start:start + n].view(B, S, h1 - h0, D))
+    return views
+
+
 def ulysses_seq2head(x: Union[torch.Tensor, Sequence[torch.Tensor]], P: int, *,
-                     out: Optional[Sequence[torch.Tensor]] = None):
+                     anything: bool = False, out: Optional[Sequence[torch.Tensor]] = None):
     """[B, S, H, D] -> [P, B, S, H/P, D] (group p = heads p*H/P .. (p+1)*H/P - 1).
 
-    Accepts one tensor or up to 8 same-shaped tensors (one launch)."""
+    Accepts one tensor or up to 8 same-shaped tensors (one launch).  With
+    ``anything`` (Ulysses Anything: H and S need not divide by P) the result
+    is a flat buffer of B*S*H*D elements per tensor, the groups back to back
+    (``ulysses_groups`` gives their views)."""
     xs, single = _as_list(x)
     if not xs:
         raise CruInvalid(1, "no tensors")
     descs = [_desc(t, f"x[{i}]") for i, t in enumerate(xs)]
     B, S, H, D = xs[0].shape
+    even = P >= 1 and H % P == 0 and not anything
     if out is None:
-        hp = H // P if P >= 1 else 0
-        ys = [torch.empty((P, B, S, hp, D), dtype=t.dtype, device=t.device) for t in xs] \
-            if P >= 1 and H % P == 0 else [torch.empty(0, dtype=t.dtype, device=t.device) for t in xs]
+        if anything:
+            ys = [torch.empty(B * S * H * D, dtype=t.dtype, device=t.device) for t in xs]
+        elif even:
+            ys = [torch.empty((P, B, S, H // P, D), dtype=t.dtype, device=t.device) for t in xs]
+        else:
+            ys = [torch.empty(0, dtype=t.dtype, device=t.device) for t in xs]
     else:
         ys, _ = _as_list(out)
     if len(ys) != len(xs):
         raise CruInvalid(1, "one output per input")
-    if P >= 1 and H % P == 0:
-        for y, t in zip(ys, xs):
-            if tuple(y.shape) != (P, B, S, H // P, D) or not y.is_contiguous() or y.dtype != t.dtype:
-                raise CruInvalid(1, f"output must be a contiguous {(P, B, S, H // P, D)} {t.dtype} tensor")
+    for y, t in zip(ys, xs):
+        if anything:
+            if y.numel() != B * S * H * D or not y.is_contiguous() or y.dtype != t.dtype:
+                raise CruInvalid(1, f"output must be a contiguous {t.dtype} buffer of "
+                                    f"{B * S * H * D} elements")
+        elif even and (tuple(y.shape) != (P, B, S, H // P, D) or not y.is_contiguous()
+                       or y.dtype != t.dtype):
+            raise CruInvalid(1, f"output must be a contiguous {(P, B, S, H // P, D)} {t.dtype} tensor")
     n = len(xs)
     xarr = (CruTensor * n)(*descs)
     yarr = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
-    _check(lib().cru_ulysses_seq2head(n, xarr, yarr, P, _stream(xs[0])))
+    _check(lib().cru_ulysses_seq2head(n, xarr, yarr, P, int(bool(anything)), _stream(xs[0])))
     return ys[0] if single else ys
 
 
 def ulysses_head2seq(y: Union[torch.Tensor, Sequence[torch.Tensor]], P: int, *,
+                     anything: bool = False, shape: Optional[Sequence[int]] = None,
                      out: Optional[Union[torch.Tensor, Sequence[torch.Tensor]]] = None):
-    """[P, B, S, H/P, D] -> [B, S, H, D]; the inverse of ulysses_seq2head."""
+    """[P, B, S, H/P, D] -> [B, S, H, D]; the inverse of ulysses_seq2head.
+
+    With ``anything`` the inputs are packed buffers as ulysses_seq2head writes
+    them, and the [B, S, H, D] shape comes from ``shape`` or ``out``."""
     ys, single = _as_list(y)
     if not ys:
         raise CruInvalid(1, "no tensors")
-    for t in ys:
-        if t.dim() != 5 or t.shape[0] != P or not t.is_contiguous():
-            raise CruInvalid(1, f"input must be a contiguous [P={P}, B, S, H/P, D] tensor")
-    _, B, S, hp, D = ys[0].shape
-    if out is None:
-        xs = [torch.empty((B, S, P * hp, D), dtype=t.dtype, device=t.device) for t in ys]
+    if anything:
+        if out is not None:
+            xs, _ = _as_list(out)
+            B, S, H, D = xs[0].shape
+        elif shape is not None:
+            B, S, H, D = (int(x) for x in shape)
+            xs = [torch.empty((B, S, H, D), dtype=t.dtype, device=t.device) for t in ys]
+        else:
+            raise CruInvalid(1, "anything=True needs the [B, S, H, D] shape (shape= or out=)")
+        for t in ys:
+            if t.numel() != B * S * H * D or not t.is_contiguous():
+                raise CruInvalid(1, f"input must be a contiguous buffer of {B * S * H * D} elements")
     else:
-        xs, _ = _as_list(out)
+        for t in ys:
+            if t.dim() != 5 or t.shape[0] != P or not t.is_contiguous():
+                raise CruInvalid(1, f"input must be a contiguous [P={P}, B, S, H/P, D] tensor")
+        _, B, S, hp, D = ys[0].shape
+        H = P * hp
+        if out is None:
+            xs = [torch.empty((B, S, H, D), dtype=t.dtype, device=t.device) for t in ys]
+        else:
+            xs, _ = _as_list(out)
+        for t in ys:
+            if tuple(t.shape) != (P, B, S, hp, D):
+                raise CruInvalid(1, "inputs must match in shape")
     if len(xs) != len(ys):
         raise CruInvalid(1, "one output per input")
     for t, x in zip(ys, xs):
-        if tuple(t.shape) != (P, B, S, hp, D) or x.dtype != t.dtype or \
-                tuple(x.shape) != (B, S, P * hp, D):
+        if x.dtype != t.dtype or tuple(x.shape) != (B, S, H, D):
             raise CruInvalid(1, "inputs and outputs must match in shape and dtype")
     n = len(ys)
     xarr = (CruTensor * n)(*[_desc(t, f"out[{i}]") for i, t in enumerate(xs)])
     yarr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in ys])
-    _check(lib().cru_ulysses_head2seq(n, yarr, xarr, P, _stream(ys[0])))
+    _check(lib().cru_ulysses_head2seq(n, yarr, xarr, P, int(bool(anything)), _stream(ys[0])))
     return xs[0] if single else xs
+
+
+def usp_workspace_bytes(q: torch.Tensor, ulysses_degree: int, ring_degree: int) -> int:
+    nbytes = ctypes.c_size_t(0)
+    _check(lib().cru_usp_workspace_bytes(_desc(q, "q"), ulysses_degree, ring_degree,
+                                         ctypes.byref(nbytes)))
+    return nbytes.value
+
+
+def usp_emulate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ulysses_degree: int,
+                ring_degree: int, *, fused: bool = False, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+                return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Unified (USP) attention on a ulysses_degree x ring_degree mesh, every
+    device's share computed on this device: the full output and LSE."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = _empty_lse(q.shape[0], q.shape[2], q.shape[1], q.device)
+    qd = _desc(q, "q")
+    if workspace is None:
+        need = usp_workspace_bytes(q, ulysses_degree, ring_degree)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    kd, vd, od, ld = _desc(k, "k"), _desc(v, "v"), _desc(out, "out"), _lse_desc(lse, "lse")
+    _check(lib().cru_usp_emulate(qd, kd, vd, ulysses_degree, ring_degree, int(bool(fused)), od,
+                                 _ref(ld), ctypes.c_float(0.0 if scale is None else scale),
+                                 workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), _stream(q)))
+    return out, lse
 
 
 # ------------------------------------------------------------- configuration
@@ -333,7 +426,8 @@ class ContextParallelConfig:
     page: degrees are >= 1; Ring Anything needs ring_degree > 1 and
     ulysses_degree == 1; Ulysses Anything needs ulysses_degree > 1 and
     ring_degree == 1.  Partials are fp32 (convert_to_fp32=True is the
-    default); bf16 partials are not implemented.
+    default); bf16 partials are not implemented.  Both degrees > 1 is
+    Unified attention (usp_emulate).
     """
     ring_degree: int = 1
     ulysses_degree: int = 1
@@ -350,5 +444,3 @@ class ContextParallelConfig:
             raise ValueError("ulysses_anything needs ulysses_degree > 1 and ring_degree == 1")
         if not self.convert_to_fp32:
             raise NotImplementedError("bf16 partial outputs (convert_to_fp32=False)")
-        if self.ulysses_anything:
-            raise NotImplementedError("Ulysses Anything (uneven head/sequence splits)")

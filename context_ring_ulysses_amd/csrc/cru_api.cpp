@@ -432,8 +432,8 @@ cru_status cru_ring_emulate(const cru_tensor* q_share, const cru_tensor* k, cons
   return hip_status(cru::launch_merge(m, stream), "ring merge launch");
 }
 
-static cru_status layout_common(int n, const cru_tensor* x, int P, const char* what,
-                                cru::LayoutArgs* a) {
+static cru_status layout_common(int n, const cru_tensor* x, int P, int anything,
+                                const char* what, cru::LayoutArgs* a) {
   if (n < 1 || n > 8) return fail(CRU_EINVAL, "%s: n = %d tensors, must be in [1, 8]", what, n);
   if (x == nullptr) return fail(CRU_EINVAL, "%s: x is NULL", what);
   for (int t = 0; t < n; ++t) {
@@ -445,11 +445,16 @@ static cru_status layout_common(int n, const cru_tensor* x, int P, const char* w
   }
   CRU_TRY(check_head_dim(&x[0], "x[0]"));
   if (P < 1) return fail(CRU_EINVAL, "%s: P = %d must be >= 1", what, P);
-  if (x[0].H % P != 0)
-    return fail(CRU_ENOTDIV, "%s: head count %lld is not divisible by Ulysses degree %d", what,
-                (long long)x[0].H, P);
-  if (x[0].S % P != 0)
-    return fail(CRU_ENOTDIV, "%s: sequence length %lld is not divisible by Ulysses degree %d",
+  if (anything != 0 && anything != 1) return fail(CRU_EINVAL, "%s: anything must be 0 or 1", what);
+  if (!anything && x[0].H % P != 0)
+    return fail(CRU_ENOTDIV,
+                "%s: head count %lld is not divisible by Ulysses degree %d "
+                "(set anything = 1 for Ulysses Anything)",
+                what, (long long)x[0].H, P);
+  if (!anything && x[0].S % P != 0)
+    return fail(CRU_ENOTDIV,
+                "%s: sequence length %lld is not divisible by Ulysses degree %d "
+                "(set anything = 1 for Ulysses Anything)",
                 what, (long long)x[0].S, P);
   CRU_TRY(check_index_range(x[0].B * x[0].S * x[0].H * x[0].D * elem_bytes(x[0].dtype) / 16 + 512,
                             what));
@@ -461,11 +466,28 @@ static cru_status layout_common(int n, const cru_tensor* x, int P, const char* w
   return CRU_OK;
 }
 
-cru_status cru_ulysses_seq2head(int n, const cru_tensor* x, void* const* y, int P,
+cru_status cru_ulysses_head_bounds(int64_t H, int P, int anything, int64_t* starts) {
+  g_err[0] = '\0';
+  if (starts == nullptr) return fail(CRU_EINVAL, "starts is NULL");
+  if (P < 1) return fail(CRU_EINVAL, "P = %d must be >= 1", P);
+  if (H < 0 || H > kMaxDim) return fail(CRU_EINVAL, "head count %lld out of range", (long long)H);
+  if (anything != 0 && anything != 1) return fail(CRU_EINVAL, "anything must be 0 or 1");
+  if (!anything && H % P != 0)
+    return fail(CRU_ENOTDIV,
+                "head count %lld is not divisible by Ulysses degree %d "
+                "(set anything = 1 for Ulysses Anything)",
+                (long long)H, P);
+  const int64_t base = H / P, extra = H % P;
+  starts[0] = 0;
+  for (int p = 0; p < P; ++p) starts[p + 1] = starts[p] + base + (p < extra ? 1 : 0);
+  return CRU_OK;
+}
+
+cru_status cru_ulysses_seq2head(int n, const cru_tensor* x, void* const* y, int P, int anything,
                                 hipStream_t stream) {
   g_err[0] = '\0';
   cru::LayoutArgs a = {};
-  CRU_TRY(layout_common(n, x, P, "seq2head", &a));
+  CRU_TRY(layout_common(n, x, P, anything, "seq2head", &a));
   if (y == nullptr) return fail(CRU_EINVAL, "seq2head: y is NULL");
   const bool empty = (int64_t)a.B * a.S * a.H * a.D == 0;
   for (int t = 0; t < n; ++t) {
@@ -485,10 +507,10 @@ cru_status cru_ulysses_seq2head(int n, const cru_tensor* x, void* const* y, int 
 }
 
 cru_status cru_ulysses_head2seq(int n, const void* const* y, const cru_tensor* x, int P,
-                                hipStream_t stream) {
+                                int anything, hipStream_t stream) {
   g_err[0] = '\0';
   cru::LayoutArgs a = {};
-  CRU_TRY(layout_common(n, x, P, "head2seq", &a));
+  CRU_TRY(layout_common(n, x, P, anything, "head2seq", &a));
   if (y == nullptr) return fail(CRU_EINVAL, "head2seq: y is NULL");
   const bool empty = (int64_t)a.B * a.S * a.H * a.D == 0;
   for (int t = 0; t < n; ++t) {
@@ -505,6 +527,110 @@ cru_status cru_ulysses_head2seq(int n, const void* const* y, const cru_tensor* x
   }
   a.dir = 1;
   return hip_status(cru::launch_layout(a, stream), "head2seq launch");
+}
+
+// Unified (USP) attention over a 2-D mesh of ulysses_degree x ring_degree
+// devices, every device's share computed on this one:
+//   1. seq2head of Q, K and V with P = ulysses_degree (the Ulysses
+//      all-to-all's net effect);
+//   2. per head group u, the ring over ring_degree sequence chunks: every
+//      query row of the group against every chunk, fp32 partials folded in
+//      ascending chunk order (rows of chunk r are ring rank r's share);
+//   3. head2seq of the group outputs (the reverse all-to-all).
+// The workspace holds the three regrouped inputs, the regrouped output and
+// one ring workspace, reused by every group.
+static size_t usp_parts(const cru_tensor* q, int Pu, int Pr, size_t* y_bytes, size_t* og_bytes,
+                        size_t* ring_bytes) {
+  const size_t elems = (size_t)q->B * q->S * q->H * q->D;
+  const size_t rows_g = (size_t)q->B * q->S * (q->H / Pu);
+  *y_bytes = align256(elems * elem_bytes(q->dtype));
+  *og_bytes = align256(elems * 4);
+  *ring_bytes = (size_t)Pr * (align256(rows_g * q->D * 4) + align256(rows_g * 4));
+  return 3 * *y_bytes + *og_bytes + *ring_bytes;
+}
+
+static cru_status usp_degrees(const cru_tensor* q, int Pu, int Pr) {
+  if (Pu < 1) return fail(CRU_EINVAL, "ulysses_degree = %d must be >= 1", Pu);
+  if (Pr < 1 || Pr > CRU_MAX_PARTS)
+    return fail(CRU_EINVAL, "ring_degree = %d, must be in [1, %d]", Pr, CRU_MAX_PARTS);
+  if (q->H % Pu != 0)
+    return fail(CRU_ENOTDIV, "head count %lld is not divisible by ulysses_degree %d",
+                (long long)q->H, Pu);
+  if (q->S % ((int64_t)Pu * Pr) != 0)
+    return fail(CRU_ENOTDIV,
+                "sequence length %lld is not divisible by ulysses_degree * ring_degree = %lld",
+                (long long)q->S, (long long)Pu * Pr);
+  return CRU_OK;
+}
+
+cru_status cru_usp_workspace_bytes(const cru_tensor* q, int ulysses_degree, int ring_degree,
+                                   size_t* bytes) {
+  g_err[0] = '\0';
+  if (bytes == nullptr) return fail(CRU_EINVAL, "bytes is NULL");
+  CRU_TRY(check_tensor(q, "q"));
+  CRU_TRY(usp_degrees(q, ulysses_degree, ring_degree));
+  size_t y, og, ring;
+  *bytes = usp_parts(q, ulysses_degree, ring_degree, &y, &og, &ring);
+  return CRU_OK;
+}
+
+cru_status cru_usp_emulate(const cru_tensor* q, const cru_tensor* k, const cru_tensor* v,
+                           int ulysses_degree, int ring_degree, int fused,
+                           const cru_tensor* o, const cru_lse* lse, float scale,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_err[0] = '\0';
+  CRU_TRY(check_qkvo(q, k, v, o));
+  if (k->S != q->S)
+    return fail(CRU_EINVAL, "USP shards one sequence: k has %lld rows, q %lld",
+                (long long)k->S, (long long)q->S);
+  if (lse != nullptr) CRU_TRY(check_lse(lse, "lse", q->B, q->H, q->S));
+  if (fused != 0 && fused != 1) return fail(CRU_EINVAL, "fused must be 0 or 1");
+  const int Pu = ulysses_degree, Pr = ring_degree;
+  CRU_TRY(usp_degrees(q, Pu, Pr));
+  float scale_log2 = 0.0f;
+  CRU_TRY(check_scale(scale, q->D, &scale_log2));
+  size_t y_bytes, og_bytes, ring_bytes;
+  const size_t need = usp_parts(q, Pu, Pr, &y_bytes, &og_bytes, &ring_bytes);
+  if (need > 0 && workspace == nullptr) return fail(CRU_EWORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(CRU_EWORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(CRU_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  if (q->B * q->S * q->H == 0) return CRU_OK;
+
+  const int64_t B = q->B, S = q->S, H = q->H, D = q->D, Hp = H / Pu;
+  char* ws = static_cast<char*>(workspace);
+  void* y[3] = {ws, ws + y_bytes, ws + 2 * y_bytes};
+  char* og = ws + 3 * y_bytes;
+  void* ring_ws = og + og_bytes;
+
+  const cru_tensor x3[3] = {*q, *k, *v};
+  CRU_TRY(cru_ulysses_seq2head(3, x3, y, Pu, 0, stream));
+
+  const int64_t group = B * S * Hp * D;    // elements of one head group
+  const int o_es = elem_bytes(o->dtype), in_es = elem_bytes(q->dtype);
+  for (int u = 0; u < Pu; ++u) {
+    cru_tensor t[3];
+    for (int i = 0; i < 3; ++i) {
+      t[i] = *q;
+      t[i].data = static_cast<char*>(y[i]) + u * group * in_es;
+      t[i].H = Hp;
+      t[i].sb = S * Hp * D; t[i].ss = Hp * D; t[i].sh = D;
+    }
+    cru_tensor og_u = t[0];
+    og_u.data = og + u * group * o_es;
+    og_u.dtype = o->dtype;
+    cru_lse lse_u;
+    if (lse != nullptr) {
+      lse_u = *lse;
+      lse_u.data = lse->data + u * Hp * lse->sh;
+      lse_u.H = Hp;
+    }
+    CRU_TRY(cru_ring_emulate(&t[0], &t[1], &t[2], Pr, 0, nullptr, fused, &og_u,
+                             lse ? &lse_u : nullptr, scale, ring_ws, ring_bytes, stream));
+  }
+  const void* og_p[1] = {og};
+  return cru_ulysses_head2seq(1, og_p, o, Pu, 0, stream);
 }
 
 }  // extern "C"

@@ -61,7 +61,10 @@ struct LayoutArgs {
   int n;
   int elem_bytes;             // 2 or 4
   int dir;
-  FastDiv div_h, div_s, div_hp, div_b;   // set by launch_layout
+  // set by launch_layout: head groups of q = H / P heads, the first rem of
+  // them one more (uneven when rem != 0)
+  int quo, rem, uneven;
+  FastDiv div_h, div_s, div_hp, div_b, div_q, div_q1;
 };
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);

@@ -19,7 +19,13 @@
  *    "Ring Anything Attention" section (chunks of unequal length).
  *  - The sequence<->head regrouping of Ulysses attention.  Same guide,
  *    "Ulysses Attention" section: the first all-to-all leaves each device
- *    with every token of a subset of heads, the second regroups by token.
+ *    with every token of a subset of heads, the second regroups by token;
+ *    "Ulysses Anything Attention" section: head count and sequence length
+ *    need not divide by the degree.
+ *  - Unified attention on a 2-D mesh of ulysses_degree x ring_degree
+ *    devices.  Same guide, "Unified Attention" section: an all-to-all
+ *    regroups heads and tokens, ring attention runs on the result, and the
+ *    reverse all-to-all restores the layout.
  *
  * Conventions shared by every entry point:
  *  - All data pointers are device memory on the current HIP device, owned by
@@ -54,7 +60,7 @@
 extern "C" {
 #endif
 
-#define CRU_ABI_VERSION 1
+#define CRU_ABI_VERSION 2
 /* Most partial results one merge (or one ring share) may fold. */
 #define CRU_MAX_PARTS 64
 
@@ -177,32 +183,86 @@ cru_status cru_ring_emulate(const cru_tensor* q_share, const cru_tensor* k,
                             size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * cru_ulysses_head_bounds -- the heads of each Ulysses group: group p holds
+ * heads [starts[p], starts[p+1]).  The first H mod P groups get one head
+ * more (sizes differ by at most one).  With anything = 0, H must be
+ * divisible by P (CRU_ENOTDIV otherwise).  Host-only; starts is a host array
+ * of P + 1 entries.
+ */
+cru_status cru_ulysses_head_bounds(int64_t H, int P, int anything, int64_t* starts);
+
+/*
  * cru_ulysses_seq2head -- the first Ulysses all-to-all's net effect on one
- * device, for n tensors in one launch:
- *   y_t[p, b, s, j, d] = x_t[b, s, p*H/P + j, d],
- * i.e. [B, S, H, D] -> [P, B, S, H/P, D]; group p holds every token of heads
- * [p*H/P, (p+1)*H/P).  A bit-exact copy.
+ * device, for n tensors in one launch.  With Hp = H / P:
+ *   y_t[p, b, s, j, d] = x_t[b, s, p*Hp + j, d],
+ * i.e. [B, S, H, D] -> [P, B, S, Hp, D]; group p holds every token of heads
+ * [p*Hp, (p+1)*Hp).  A bit-exact copy.
  *
- *   x   host array of n views, all the same shape and dtype (bf16 or fp32)
- *   y   host array of n device pointers to contiguous [P, B, S, H/P, D]
- *       buffers of that dtype, 16-byte aligned, not overlapping any x
- *   1 <= n <= 8;  P >= 1 must divide H and S (CRU_ENOTDIV otherwise: the
- *   sequence is sharded P ways before the exchange).
+ *   x         host array of n views, all the same shape and dtype (bf16 or
+ *             fp32)
+ *   y         host array of n device pointers to contiguous buffers of
+ *             B*S*H*D elements of that dtype, 16-byte aligned, not
+ *             overlapping any x
+ *   1 <= n <= 8;  P >= 1
+ *   anything  0: P must divide H and S (CRU_ENOTDIV otherwise: the sequence
+ *                is sharded P ways before the exchange);
+ *             1: any H and S ("Ulysses Anything").  Groups follow
+ *                cru_ulysses_head_bounds and lie back to back: group p is a
+ *                contiguous [B, S, Hp_p, D] block at element B*S*D*starts[p]
+ *                (which is the [P, B, S, Hp, D] layout when P divides H).
  */
 cru_status cru_ulysses_seq2head(int n, const cru_tensor* x, void* const* y,
-                                int P, hipStream_t stream);
+                                int P, int anything, hipStream_t stream);
 
 /*
  * cru_ulysses_head2seq -- the inverse regrouping (the second all-to-all):
- *   x_t[b, s, p*H/P + j, d] = y_t[p, b, s, j, d].
+ *   x_t[b, s, p*Hp + j, d] = y_t[p, b, s, j, d]   (and likewise for uneven
+ *   groups).
  *
- *   y   host array of n device pointers to contiguous [P, B, S, H/P, D]
+ *   y   host array of n device pointers to packed buffers laid out as
+ *       cru_ulysses_seq2head writes them
  *   x   host array of n output views [B, S, H, D] (shape, dtype, strides)
  *   same rules as cru_ulysses_seq2head.
  */
 cru_status cru_ulysses_head2seq(int n, const void* const* y,
-                                const cru_tensor* x, int P,
+                                const cru_tensor* x, int P, int anything,
                                 hipStream_t stream);
+
+/*
+ * cru_usp_workspace_bytes -- bytes of device workspace cru_usp_emulate needs
+ * for q's shape and the two degrees (the same size serves bf16 and fp32
+ * outputs).  Same divisibility rules as cru_usp_emulate.
+ */
+cru_status cru_usp_workspace_bytes(const cru_tensor* q, int ulysses_degree,
+                                   int ring_degree, size_t* bytes);
+
+/*
+ * cru_usp_emulate -- Unified (USP) attention over a 2-D mesh of
+ * ulysses_degree x ring_degree devices, every device's share computed on
+ * this one, with the full output and LSE as the result:
+ *   1. seq2head of q, k, v with P = ulysses_degree;
+ *   2. for each head group u, the ring over ring_degree equal sequence
+ *      chunks: every query row of the group against every chunk, the fp32
+ *      partials folded in ascending chunk order (the rows of chunk r are
+ *      ring rank r's share; fused selects one split-KV launch per group as
+ *      in cru_ring_emulate);
+ *   3. head2seq of the group outputs into o.
+ *
+ *   q, k, v   [B, S, H, D] bf16 or fp32, one sequence (k and v have q's S)
+ *   ulysses_degree >= 1 must divide H, and ulysses_degree * ring_degree
+ *   must divide S (CRU_ENOTDIV otherwise: the sequence is sharded over the
+ *   whole mesh; the Anything variants do not combine with Unified attention);
+ *   1 <= ring_degree <= CRU_MAX_PARTS
+ *   o         [B, S, H, D] bf16 or fp32;  lse [B, H, S] fp32 or NULL
+ *   scale     as for cru_attn_fwd_lse
+ *   workspace device memory of at least cru_usp_workspace_bytes(), 256-byte
+ *             aligned, not overlapping any argument
+ */
+cru_status cru_usp_emulate(const cru_tensor* q, const cru_tensor* k,
+                           const cru_tensor* v, int ulysses_degree,
+                           int ring_degree, int fused, const cru_tensor* o,
+                           const cru_lse* lse, float scale, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
 
 /* Name of a status code (static storage). */
 const char* cru_status_str(int status);

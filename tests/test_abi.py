@@ -47,7 +47,7 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L_ = cru.lib()
-    assert L_.cru_abi_version() == 1
+    assert L_.cru_abi_version() == 2
     names = [L_.cru_status_str(i).decode() for i in range(7)]
     assert names == ["CRU_OK", "CRU_EINVAL", "CRU_ENOTDIV", "CRU_EUNSUPPORTED",
                      "CRU_EDEVICE", "CRU_EWORKSPACE", "CRU_EHIP"]
@@ -208,18 +208,18 @@ def test_ring_validation():
     assert ring(qf, kf, vf, 4, o=T(S=10)) == EUNSUPPORTED
 
 
-def s2h(xs, P, ys=None):
+def s2h(xs, P, ys=None, anything=0):
     n = len(xs)
     X = (cru.CruTensor * n)(*xs)
     Y = (ctypes.c_void_p * n)(*(ys or [FAKE * 8] * n))
-    return cru.lib().cru_ulysses_seq2head(n, X, Y, P, None)
+    return cru.lib().cru_ulysses_seq2head(n, X, Y, P, anything, None)
 
 
-def h2s(xs, P, ys=None):
+def h2s(xs, P, ys=None, anything=0):
     n = len(xs)
     X = (cru.CruTensor * n)(*xs)
     Y = (ctypes.c_void_p * n)(*(ys or [FAKE * 8] * n))
-    return cru.lib().cru_ulysses_head2seq(n, Y, X, P, None)
+    return cru.lib().cru_ulysses_head2seq(n, Y, X, P, anything, None)
 
 
 def test_ulysses_validation():
@@ -235,6 +235,59 @@ def test_ulysses_validation():
     assert s2h([x], 2) == EDEVICE                 # passes host checks
     assert h2s([x], 4) == ENOTDIV
     assert h2s([x], 2) == EDEVICE
+    # Ulysses Anything: uneven heads and tokens pass the host checks
+    assert s2h([x], 4, anything=1) == EDEVICE
+    assert s2h([T(S=15, H=6)], 2, anything=1) == EDEVICE
+    assert h2s([T(S=15, H=7)], 3, anything=1) == EDEVICE
+    assert s2h([x], 7, anything=1) == EDEVICE     # more groups than heads: some are empty
+    assert s2h([x], 2, anything=2) == EINVAL
+
+
+def head_bounds(H, P, anything):
+    starts = (ctypes.c_int64 * (P + 1))()
+    st = cru.lib().cru_ulysses_head_bounds(H, P, anything, starts)
+    return st, [(starts[p], starts[p + 1]) for p in range(P)]
+
+
+def test_head_bounds():
+    assert head_bounds(24, 2, 0) == (OK, [(0, 12), (12, 24)])
+    assert head_bounds(30, 4, 0)[0] == ENOTDIV
+    assert head_bounds(30, 4, 1) == (OK, [(0, 8), (8, 16), (16, 23), (23, 30)])
+    assert head_bounds(3, 5, 1) == (OK, [(0, 1), (1, 2), (2, 3), (3, 3), (3, 3)])
+    assert head_bounds(8, 0, 1)[0] == EINVAL
+    for H in range(0, 40):
+        for P in range(1, 9):
+            st, b = head_bounds(H, P, 1)
+            assert st == OK and b == oracle.chunk_bounds(H, P)   # the same near-equal rule
+    assert cru.ulysses_head_bounds(30, 4, anything=True)[2] == (16, 23)
+
+
+def usp(q, k, v, Pu, Pr, fused=0, o=None, ws=FAKE * 4, ws_bytes=1 << 40):
+    o = o or T(S=q.S, H=q.H, D=q.D, dtype=q.dtype)
+    return cru.lib().cru_usp_emulate(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), Pu, Pr,
+                                     fused, ctypes.byref(o), None, ctypes.c_float(0.0), ws,
+                                     ws_bytes, None)
+
+
+def test_usp_validation():
+    q = T(S=16, H=4)
+    assert usp(q, q, q, 2, 2) == EDEVICE                     # passes host checks
+    assert usp(T(S=16, H=6), T(S=16, H=6), T(S=16, H=6), 4, 2) == ENOTDIV   # H % Pu
+    assert usp(T(S=12, H=4), T(S=12, H=4), T(S=12, H=4), 2, 4) == ENOTDIV   # S % (Pu Pr)
+    assert "ulysses_degree * ring_degree" in last_error()
+    assert usp(q, T(S=8, H=4), T(S=8, H=4), 2, 2) == EINVAL  # one sequence: Skv == Sq
+    assert usp(q, q, q, 0, 2) == EINVAL
+    assert usp(q, q, q, 2, 0) == EINVAL
+    assert usp(q, q, q, 2, 2, fused=2) == EINVAL
+    assert usp(q, q, q, 2, 2, ws=0) == EWORKSPACE
+    need = ctypes.c_size_t(0)
+    assert cru.lib().cru_usp_workspace_bytes(ctypes.byref(q), 2, 2, ctypes.byref(need)) == OK
+    a256 = lambda x: (x + 255) // 256 * 256
+    elems = 1 * 16 * 4 * 64
+    rows_g = 1 * 16 * 2
+    assert need.value == 3 * a256(elems * 2) + a256(elems * 4) + 2 * (a256(rows_g * 64 * 4) + a256(rows_g * 4))
+    assert usp(q, q, q, 2, 2, ws_bytes=need.value - 1) == EWORKSPACE
+    assert usp(q, q, q, 2, 2, ws_bytes=need.value) == EDEVICE
 
 
 def test_config_rules():
@@ -251,6 +304,7 @@ def test_config_rules():
         C(ring_degree=1, ring_anything=True)
     with pytest.raises(ValueError):
         C(ulysses_degree=2, ring_degree=2, ulysses_anything=True)
+    C(ulysses_degree=4, ulysses_anything=True)
     with pytest.raises(NotImplementedError):
         C(ring_degree=2, convert_to_fp32=False)
 
