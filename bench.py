@@ -269,7 +269,47 @@ def main():
                        "GB/s": 2 * tbytes / (med2 * 1e-3) / 1e9,
                        "frac_hbm_peak": 2 * tbytes / (med2 * 1e-3) / 1e9 / PEAK_HBM_GBS,
                        "plain_copy_same_bytes_GB/s": 2 * tbytes / (medc2 * 1e-3) / 1e9}}
-    del qv, kv_, vv, ysv, ov, scrub, sink
+    # Ulysses Anything: the video shape at degree 4 (30 heads -> groups of 8, 8, 7, 7)
+    Pa = 4
+    ysa = [torch.empty(qv.numel(), dtype=qv.dtype, device=dev) for _ in range(3)]
+    meda1, _ = cold(lambda: cru.ulysses_seq2head([qv, kv_, vv], Pa, anything=True, out=ysa),
+                    args.cold_reps)
+    meda2, _ = cold(lambda: cru.ulysses_head2seq(ysa[0], Pa, anything=True, out=ov),
+                    args.cold_reps)
+    anything_layout = {
+        "workload": "video-dit-4276 (B=2, S=4276, H=30, D=64, bf16), P=4: head groups 8,8,7,7",
+        "seq2head_qkv": {"bytes": 6 * tbytes, "ms_median": meda1,
+                         "GB/s": 6 * tbytes / (meda1 * 1e-3) / 1e9,
+                         "frac_hbm_peak": 6 * tbytes / (meda1 * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "head2seq_o": {"bytes": 2 * tbytes, "ms_median": meda2,
+                       "GB/s": 2 * tbytes / (meda2 * 1e-3) / 1e9,
+                       "frac_hbm_peak": 2 * tbytes / (meda2 * 1e-3) / 1e9 / PEAK_HBM_GBS}}
+    del qv, kv_, vv, ysv, ov, ysa, scrub, sink
+    torch.cuda.synchronize()
+
+    # Unified attention: FLUX-1024 on a 2 (Ulysses) x 4 (ring) mesh, every
+    # device's share on this GPU (seq2head, a fused ring share per head group,
+    # head2seq), timed warm like the step
+    Pu, Pr = 2, 4
+    usp_ws = torch.empty(cru.usp_workspace_bytes(q, Pu, Pr), dtype=torch.uint8, device=dev)
+    o_usp = torch.empty_like(q)
+    l_usp = torch.empty(B, H, S, dtype=torch.float32, device=dev)
+    run_usp = lambda: cru.usp_emulate(q, k, v, Pu, Pr, fused=True, out=o_usp, lse=l_usp,
+                                      workspace=usp_ws)
+    for _ in range(3):
+        run_usp()
+    ts = []
+    for _ in range(20):
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        run_usp()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    usp_ms = statistics.median(ts)
+    usp = {"workload": f"flux-1024, ulysses {Pu} x ring {Pr}, all devices' shares, fused ring",
+           "ms_median": usp_ms, "TFLOP/s": f_full / (usp_ms * 1e-3) / 1e12}
+    del usp_ws, o_usp, l_usp
     torch.cuda.synchronize()
 
     traffic = counters_traffic()
@@ -297,6 +337,8 @@ def main():
                    "step_attention_flops": step_flops},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "usp": usp,
+        "ulysses_anything_cold_layout": anything_layout,
         "parts_ms": part_ms,
         "attn_full_tflops": attn_tflops,
         "attn_full_frac_bf16_peak": attn_tflops / PEAK_BF16_TFLOPS,
