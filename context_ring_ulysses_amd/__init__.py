@@ -113,7 +113,8 @@ def lib() -> ctypes.CDLL:
     L.cru_ring_workspace_bytes.argtypes = [T, ctypes.c_int, _P(ctypes.c_size_t)]
     L.cru_ring_workspace_bytes.restype = st
     L.cru_ring_emulate.argtypes = [T, T, T, ctypes.c_int, ctypes.c_int, _P(ctypes.c_int64),
-                                   ctypes.c_int, T, Lse, ctypes.c_float, vp, ctypes.c_size_t, vp]
+                                   ctypes.c_int, ctypes.c_int, T, Lse, ctypes.c_float, vp,
+                                   ctypes.c_size_t, vp]
     L.cru_ring_emulate.restype = st
     L.cru_ulysses_head_bounds.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                           _P(ctypes.c_int64)]
@@ -124,8 +125,8 @@ def lib() -> ctypes.CDLL:
     L.cru_ulysses_head2seq.restype = st
     L.cru_usp_workspace_bytes.argtypes = [T, ctypes.c_int, ctypes.c_int, _P(ctypes.c_size_t)]
     L.cru_usp_workspace_bytes.restype = st
-    L.cru_usp_emulate.argtypes = [T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int, T, Lse,
-                                  ctypes.c_float, vp, ctypes.c_size_t, vp]
+    L.cru_usp_emulate.argtypes = [T, T, T, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, T, Lse, ctypes.c_float, vp, ctypes.c_size_t, vp]
     L.cru_usp_emulate.restype = st
     L.cru_status_str.argtypes = [ctypes.c_int]
     L.cru_status_str.restype = ctypes.c_char_p
@@ -244,11 +245,15 @@ def ring_workspace_bytes(q_share: torch.Tensor, n_chunks: int) -> int:
 
 def ring_emulate(q_share: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_chunks: int, *,
                  anything: bool = False, chunk_sizes: Optional[Sequence[int]] = None,
-                 fused: bool = False, out: Optional[torch.Tensor] = None,
+                 fused: bool = False, convert_to_fp32: bool = True,
+                 out: Optional[torch.Tensor] = None,
                  lse: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
                  scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
                  return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """One ring rank's share: q_share against every K/V chunk, folded in order."""
+    """One ring rank's share: q_share against every K/V chunk, folded in order.
+
+    ``convert_to_fp32=False`` keeps each chunk's partial output in bf16 (the
+    partial LSEs stay fp32)."""
     if out is None:
         out = torch.empty(q_share.shape, dtype=out_dtype or q_share.dtype, device=q_share.device)
     if lse is None and return_lse:
@@ -264,7 +269,7 @@ def ring_emulate(q_share: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_chun
             raise CruInvalid(1, f"{len(chunk_sizes)} chunk sizes for {n_chunks} chunks")
     kd, vd, od, ld = _desc(k, "k"), _desc(v, "v"), _desc(out, "out"), _lse_desc(lse, "lse")
     _check(lib().cru_ring_emulate(qd, kd, vd, n_chunks, int(bool(anything)), sizes,
-                                  int(bool(fused)), od, _ref(ld),
+                                  int(bool(fused)), int(bool(convert_to_fp32)), od, _ref(ld),
                                   ctypes.c_float(0.0 if scale is None else scale),
                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                   _stream(q_share)))
@@ -393,7 +398,8 @@ def usp_workspace_bytes(q: torch.Tensor, ulysses_degree: int, ring_degree: int) 
 
 
 def usp_emulate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ulysses_degree: int,
-                ring_degree: int, *, fused: bool = False, out: Optional[torch.Tensor] = None,
+                ring_degree: int, *, fused: bool = False, convert_to_fp32: bool = True,
+                out: Optional[torch.Tensor] = None,
                 lse: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
                 scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
                 return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
@@ -408,7 +414,8 @@ def usp_emulate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ulysses_degre
         need = usp_workspace_bytes(q, ulysses_degree, ring_degree)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     kd, vd, od, ld = _desc(k, "k"), _desc(v, "v"), _desc(out, "out"), _lse_desc(lse, "lse")
-    _check(lib().cru_usp_emulate(qd, kd, vd, ulysses_degree, ring_degree, int(bool(fused)), od,
+    _check(lib().cru_usp_emulate(qd, kd, vd, ulysses_degree, ring_degree, int(bool(fused)),
+                                 int(bool(convert_to_fp32)), od,
                                  _ref(ld), ctypes.c_float(0.0 if scale is None else scale),
                                  workspace.data_ptr(),
                                  workspace.numel() * workspace.element_size(), _stream(q)))
@@ -425,9 +432,9 @@ class ContextParallelConfig:
     Rules from the "Context parallelism" guide's variant table and the API
     page: degrees are >= 1; Ring Anything needs ring_degree > 1 and
     ulysses_degree == 1; Ulysses Anything needs ulysses_degree > 1 and
-    ring_degree == 1.  Partials are fp32 (convert_to_fp32=True is the
-    default); bf16 partials are not implemented.  Both degrees > 1 is
-    Unified attention (usp_emulate).
+    ring_degree == 1.  Partials are fp32 with convert_to_fp32=True (the
+    default) and bf16 otherwise (ring_emulate / usp_emulate take the same
+    flag).  Both degrees > 1 is Unified attention (usp_emulate).
     """
     ring_degree: int = 1
     ulysses_degree: int = 1
@@ -442,5 +449,3 @@ class ContextParallelConfig:
             raise ValueError("ring_anything needs ring_degree > 1 and ulysses_degree == 1")
         if self.ulysses_anything and (self.ulysses_degree < 2 or self.ring_degree != 1):
             raise ValueError("ulysses_anything needs ulysses_degree > 1 and ring_degree == 1")
-        if not self.convert_to_fp32:
-            raise NotImplementedError("bf16 partial outputs (convert_to_fp32=False)")

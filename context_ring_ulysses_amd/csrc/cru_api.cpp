@@ -258,9 +258,9 @@ cru_status cru_attn_merge_lse(int n, const cru_tensor* o_parts, const cru_lse* l
   for (int c = 0; c < n; ++c) {
     const cru_tensor* p = &o_parts[c];
     CRU_TRY(check_tensor(p, "o_parts[c]"));
-    if (p->dtype != CRU_F32)
-      return fail(CRU_EUNSUPPORTED, "o_parts[%d] is %s; partial outputs are fp32", c,
-                  dtype_name(p->dtype));
+    if (p->dtype != p0->dtype)
+      return fail(CRU_EUNSUPPORTED, "o_parts[%d] is %s, o_parts[0] %s; parts share one dtype", c,
+                  dtype_name(p->dtype), dtype_name(p0->dtype));
     if (!same_shape(p, p0)) return fail(CRU_EINVAL, "o_parts[%d] shape differs from o_parts[0]", c);
     if (p->sb != p0->sb || p->ss != p0->ss || p->sh != p0->sh)
       return fail(CRU_EINVAL, "o_parts[%d] strides differ from o_parts[0]", c);
@@ -283,9 +283,10 @@ cru_status cru_attn_merge_lse(int n, const cru_tensor* o_parts, const cru_lse* l
 
   cru::MergeArgs a = {};
   for (int c = 0; c < n; ++c) {
-    a.o_part[c] = static_cast<const float*>(o_parts[c].data);
+    a.o_part[c] = o_parts[c].data;
     a.l_part[c] = lse_parts[c].data;
   }
+  a.p_bf16 = p0->dtype == CRU_BF16;
   a.p_sb = p0->sb; a.p_ss = p0->ss; a.p_sh = p0->sh;
   a.pl_sb = lse_parts[0].sb; a.pl_sh = lse_parts[0].sh;
   a.o = o->data;
@@ -330,8 +331,9 @@ cru_status cru_ring_chunk_bounds(int64_t S, int n, int anything, int64_t* starts
 
 cru_status cru_ring_emulate(const cru_tensor* q_share, const cru_tensor* k, const cru_tensor* v,
                             int n_chunks, int anything, const int64_t* chunk_sizes, int fused,
-                            const cru_tensor* o, const cru_lse* lse, float scale,
-                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                            int convert_to_fp32, const cru_tensor* o, const cru_lse* lse,
+                            float scale, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
   g_err[0] = '\0';
   CRU_TRY(check_qkvo(q_share, k, v, o));
   if (lse != nullptr) CRU_TRY(check_lse(lse, "lse", q_share->B, q_share->H, q_share->S));
@@ -339,6 +341,10 @@ cru_status cru_ring_emulate(const cru_tensor* q_share, const cru_tensor* k, cons
     return fail(CRU_EINVAL, "n_chunks = %d, must be in [1, %d]", n_chunks, CRU_MAX_PARTS);
   if (anything != 0 && anything != 1) return fail(CRU_EINVAL, "anything must be 0 or 1");
   if (fused != 0 && fused != 1) return fail(CRU_EINVAL, "fused must be 0 or 1");
+  if (convert_to_fp32 != 0 && convert_to_fp32 != 1)
+    return fail(CRU_EINVAL, "convert_to_fp32 must be 0 or 1");
+  if (!convert_to_fp32 && q_share->dtype != CRU_BF16)
+    return fail(CRU_EUNSUPPORTED, "partials in the model dtype need bf16 inputs");
   float scale_log2 = 0.0f;
   CRU_TRY(check_scale(scale, q_share->D, &scale_log2));
   CRU_TRY(check_attn_grid(n_chunks, q_share));
@@ -380,9 +386,11 @@ cru_status cru_ring_emulate(const cru_tensor* q_share, const cru_tensor* k, cons
   if (lse != nullptr) CRU_TRY(check_device(lse->data, "lse"));
   CRU_TRY(check_device(workspace, "workspace"));
 
-  // Partials in the workspace: n fp32 [B, Sq, H, D] outputs, then n [B, H, Sq] LSEs.
+  // Partials in the workspace: n [B, Sq, H, D] outputs (fp32, or bf16 without
+  // convert_to_fp32), then n fp32 [B, H, Sq] LSEs.
   const int64_t B = q_share->B, Sq = q_share->S, H = q_share->H, D = q_share->D;
-  const size_t obytes = align256((size_t)rows * D * 4);
+  const int pes = convert_to_fp32 ? 4 : 2;
+  const size_t obytes = align256((size_t)rows * D * pes);
   const size_t lbytes = align256((size_t)rows * 4);
   char* ws = static_cast<char*>(workspace);
   float* o_base = reinterpret_cast<float*>(ws);
@@ -392,13 +400,13 @@ cru_status cru_ring_emulate(const cru_tensor* q_share, const cru_tensor* k, cons
   fill_attn_views(a, q_share, k, v);
   a.o_sb = Sq * H * D; a.o_ss = H * D; a.o_sh = D;
   a.l_sb = H * Sq; a.l_sh = Sq;
-  a.o_f32 = 1;
+  a.o_f32 = convert_to_fp32;
   a.scale_log2 = scale_log2;
   auto launch = q_share->dtype == CRU_BF16 ? cru::launch_attn_bf16 : cru::launch_attn_f32;
   if (fused) {
     a.o = o_base;
     a.lse = l_base;
-    a.o_split_stride = (int64_t)(obytes / 4);
+    a.o_split_stride = (int64_t)(obytes / pes);
     a.l_split_stride = (int64_t)(lbytes / 4);
     a.n_split = n_chunks;
     for (int c = 0; c <= n_chunks; ++c) a.split_start[c] = (int)start[c];
@@ -415,8 +423,9 @@ cru_status cru_ring_emulate(const cru_tensor* q_share, const cru_tensor* k, cons
   }
 
   cru::MergeArgs m = {};
+  m.p_bf16 = !convert_to_fp32;
   for (int c = 0; c < n_chunks; ++c) {
-    m.o_part[c] = reinterpret_cast<const float*>(ws + c * obytes);
+    m.o_part[c] = ws + c * obytes;
     m.l_part[c] = reinterpret_cast<const float*>(reinterpret_cast<char*>(l_base) + c * lbytes);
   }
   m.p_sb = Sq * H * D; m.p_ss = H * D; m.p_sh = D;
@@ -575,7 +584,7 @@ cru_status cru_usp_workspace_bytes(const cru_tensor* q, int ulysses_degree, int 
 }
 
 cru_status cru_usp_emulate(const cru_tensor* q, const cru_tensor* k, const cru_tensor* v,
-                           int ulysses_degree, int ring_degree, int fused,
+                           int ulysses_degree, int ring_degree, int fused, int convert_to_fp32,
                            const cru_tensor* o, const cru_lse* lse, float scale,
                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
   g_err[0] = '\0';
@@ -585,6 +594,10 @@ cru_status cru_usp_emulate(const cru_tensor* q, const cru_tensor* k, const cru_t
                 (long long)k->S, (long long)q->S);
   if (lse != nullptr) CRU_TRY(check_lse(lse, "lse", q->B, q->H, q->S));
   if (fused != 0 && fused != 1) return fail(CRU_EINVAL, "fused must be 0 or 1");
+  if (convert_to_fp32 != 0 && convert_to_fp32 != 1)
+    return fail(CRU_EINVAL, "convert_to_fp32 must be 0 or 1");
+  if (!convert_to_fp32 && q->dtype != CRU_BF16)
+    return fail(CRU_EUNSUPPORTED, "partials in the model dtype need bf16 inputs");
   const int Pu = ulysses_degree, Pr = ring_degree;
   CRU_TRY(usp_degrees(q, Pu, Pr));
   float scale_log2 = 0.0f;
@@ -626,7 +639,7 @@ cru_status cru_usp_emulate(const cru_tensor* q, const cru_tensor* k, const cru_t
       lse_u.data = lse->data + u * Hp * lse->sh;
       lse_u.H = Hp;
     }
-    CRU_TRY(cru_ring_emulate(&t[0], &t[1], &t[2], Pr, 0, nullptr, fused, &og_u,
+    CRU_TRY(cru_ring_emulate(&t[0], &t[1], &t[2], Pr, 0, nullptr, fused, convert_to_fp32, &og_u,
                              lse ? &lse_u : nullptr, scale, ring_ws, ring_bytes, stream));
   }
   const void* og_p[1] = {og};

@@ -36,7 +36,7 @@ struct AttnArgs {
 
 // Every part shares one set of strides (checked on the host).
 struct MergeArgs {
-  const float* o_part[CRU_MAX_PARTS];
+  const void* o_part[CRU_MAX_PARTS];   // fp32, or bf16 when p_bf16
   const float* l_part[CRU_MAX_PARTS];
   int64_t p_sb, p_ss, p_sh;
   int64_t pl_sb, pl_sh;
@@ -47,6 +47,7 @@ struct MergeArgs {
   int B, S, H, D;
   int n;
   int o_f32;
+  int p_bf16;                 // partial outputs in bf16 (convert_to_fp32 off)
   FastDiv div_s, div_h;       // set by launch_merge
 };
 

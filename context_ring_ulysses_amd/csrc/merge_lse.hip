@@ -9,6 +9,10 @@
 // which equals sum_c e^{LSE_c - LSE} O_c; the sums run over c in ascending
 // order.  Parts with LSE_c = -inf hold no keys (w_c = 0, their O_c unused).
 //
+// Partial outputs are fp32 (the default, ContextParallelConfig's
+// convert_to_fp32) or bf16, the model dtype, when that conversion is off;
+// the LSEs are fp32 either way and the sums are fp32.
+//
 // Memory-bound: each part's O row is read once, O and LSE written once.
 // One thread owns VPT float4 groups of one row.  Rows are ordered (b, s, h)
 // with h fastest, the order of [B, S, H, D] memory, so a workgroup reads one
@@ -26,6 +30,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16;
 
 constexpr int kThreads = 256;
@@ -53,6 +58,19 @@ __device__ __forceinline__ RowPos row_pos(const MergeArgs& a) {
   return p;
 }
 
+// 4 elements of a partial output, as fp32
+template <bool PBF16>
+__device__ __forceinline__ f32x4 load4(const void* base, int64_t off) {
+  if constexpr (PBF16) {
+    const u16x4 x = *reinterpret_cast<const u16x4*>(static_cast<const u16*>(base) + off);
+    // bf16 -> fp32 is exact: the bf16 bits are the high half of the fp32 bits
+    return f32x4{__uint_as_float((unsigned)x[0] << 16), __uint_as_float((unsigned)x[1] << 16),
+                 __uint_as_float((unsigned)x[2] << 16), __uint_as_float((unsigned)x[3] << 16)};
+  } else {
+    return *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + off);
+  }
+}
+
 template <int VPT, bool OF32>
 __device__ __forceinline__ void store_row(const MergeArgs& a, const RowPos& p,
                                           const f32x4 (&acc)[VPT], float inv, float lse) {
@@ -72,7 +90,7 @@ __device__ __forceinline__ void store_row(const MergeArgs& a, const RowPos& p,
 }
 
 // n <= NMAX parts, everything in registers.
-template <int NMAX, int VPT, bool OF32>
+template <int NMAX, int VPT, bool OF32, bool PBF16>
 __global__ void __launch_bounds__(kThreads) merge_small(const MergeArgs a) {
   const RowPos p = row_pos<VPT>(a);
   if (!p.live) return;
@@ -88,8 +106,7 @@ __global__ void __launch_bounds__(kThreads) merge_small(const MergeArgs a) {
   for (int c = 0; c < NMAX; ++c)
 #pragma unroll
     for (int u = 0; u < VPT; ++u)
-      x[c][u] = c < a.n ? reinterpret_cast<const f32x4*>(a.o_part[c] + ooff)[u]
-                        : f32x4{0.f, 0.f, 0.f, 0.f};
+      x[c][u] = c < a.n ? load4<PBF16>(a.o_part[c], ooff + 4 * u) : f32x4{0.f, 0.f, 0.f, 0.f};
 
   float M = l[0];
 #pragma unroll
@@ -117,7 +134,7 @@ __global__ void __launch_bounds__(kThreads) merge_small(const MergeArgs a) {
 }
 
 // Any n: a first pass over the LSEs for the max, then batches of kBatch parts.
-template <bool OF32>
+template <bool OF32, bool PBF16>
 __global__ void __launch_bounds__(kThreads) merge_many(const MergeArgs a) {
   const RowPos p = row_pos<1>(a);
   if (!p.live) return;
@@ -143,8 +160,7 @@ __global__ void __launch_bounds__(kThreads) merge_many(const MergeArgs a) {
       for (int u = 0; u < kBatch; ++u) {
         const bool in = c0 + u < a.n;
         l[u] = in ? a.l_part[c0 + u][loff] : -__builtin_inff();
-        x[u] = in ? *reinterpret_cast<const f32x4*>(a.o_part[c0 + u] + ooff)
-                  : f32x4{0.f, 0.f, 0.f, 0.f};
+        x[u] = in ? load4<PBF16>(a.o_part[c0 + u], ooff) : f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
@@ -162,24 +178,25 @@ __global__ void __launch_bounds__(kThreads) merge_many(const MergeArgs a) {
   store_row<1, OF32>(a, p, acc, inv, lse);
 }
 
-template <int NMAX, bool OF32>
+template <int NMAX, bool OF32, bool PBF16>
 hipError_t launch_small(const MergeArgs& a, hipStream_t stream) {
   constexpr int VPT = 1;
   const int64_t threads = (int64_t)a.B * a.H * a.S * (a.D / 4 / VPT);
   const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
-  hipLaunchKernelGGL((merge_small<NMAX, VPT, OF32>), dim3(blocks), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((merge_small<NMAX, VPT, OF32, PBF16>), dim3(blocks), dim3(kThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
-template <bool OF32>
+template <bool OF32, bool PBF16>
 hipError_t launch_of(const MergeArgs& a, hipStream_t stream) {
-  if (a.n <= 2) return launch_small<2, OF32>(a, stream);
-  if (a.n <= 4) return launch_small<4, OF32>(a, stream);
-  if (a.n <= 8) return launch_small<8, OF32>(a, stream);
-  if (a.n <= 16) return launch_small<16, OF32>(a, stream);
+  if (a.n <= 2) return launch_small<2, OF32, PBF16>(a, stream);
+  if (a.n <= 4) return launch_small<4, OF32, PBF16>(a, stream);
+  if (a.n <= 8) return launch_small<8, OF32, PBF16>(a, stream);
+  if (a.n <= 16) return launch_small<16, OF32, PBF16>(a, stream);
   const int64_t threads = (int64_t)a.B * a.H * a.S * (a.D / 4);
   const unsigned blocks = (unsigned)((threads + kThreads - 1) / kThreads);
-  hipLaunchKernelGGL((merge_many<OF32>), dim3(blocks), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((merge_many<OF32, PBF16>), dim3(blocks), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -191,7 +208,8 @@ hipError_t launch_merge(const MergeArgs& args, hipStream_t stream) {
   MergeArgs a = args;
   a.div_s = make_fastdiv((uint32_t)a.S);
   a.div_h = make_fastdiv((uint32_t)a.H);
-  return a.o_f32 ? launch_of<true>(a, stream) : launch_of<false>(a, stream);
+  if (a.p_bf16) return a.o_f32 ? launch_of<true, true>(a, stream) : launch_of<false, true>(a, stream);
+  return a.o_f32 ? launch_of<true, false>(a, stream) : launch_of<false, false>(a, stream);
 }
 
 }  // namespace cru

@@ -121,8 +121,10 @@ cru_status cru_attn_fwd_lse(const cru_tensor* q, const cru_tensor* k,
  * A part with LSE_c = -inf holds no keys and contributes nothing; rows where
  * every part is empty give O = 0, LSE = -inf.
  *
- *   o_parts    host array of n fp32 [B, S, H, D] views, all the same shape
- *              and strides
+ *   o_parts    host array of n [B, S, H, D] views, all the same shape, strides
+ *              and dtype: fp32, or bf16 (partials kept in the model dtype,
+ *              ContextParallelConfig.convert_to_fp32 = False); the sums are
+ *              fp32 either way
  *   lse_parts  host array of n fp32 [B, H, S] LSE views, all the same strides
  *   o          [B, S, H, D] bf16 or fp32
  *   lse        [B, H, S] fp32, or NULL
@@ -137,7 +139,7 @@ cru_status cru_attn_merge_lse(int n, const cru_tensor* o_parts,
  * cru_ring_workspace_bytes -- bytes of device workspace cru_ring_emulate
  * needs for a query share shaped like q_share cut into n_chunks chunks
  * (n_chunks fp32 partial outputs and LSEs).  The same size serves both the
- * step-wise and the fused schedule.
+ * step-wise and the fused schedule, and bf16 partials (which use less).
  */
 cru_status cru_ring_workspace_bytes(const cru_tensor* q_share, int n_chunks,
                                     size_t* bytes);
@@ -169,6 +171,11 @@ cru_status cru_ring_chunk_bounds(int64_t S, int n, int anything, int64_t* starts
  *                extra row); with anything = 0 they must all be equal
  *   fused        0: one attention launch per chunk (the ring's step order);
  *                1: one launch over every (chunk, query tile, head)
+ *   convert_to_fp32  1: fp32 partial outputs (ContextParallelConfig's
+ *                default); 0: partial outputs in the model dtype, bf16
+ *                (bf16 inputs only, CRU_EUNSUPPORTED otherwise).  The
+ *                partial LSEs are fp32 either way ("Parallelism" API page,
+ *                convert_to_fp32)
  *   o            [B, Sq, H, D] bf16 or fp32;  lse [B, H, Sq] fp32 or NULL
  *   scale        as for cru_attn_fwd_lse
  *   workspace    device memory of at least cru_ring_workspace_bytes(),
@@ -178,7 +185,8 @@ cru_status cru_ring_chunk_bounds(int64_t S, int n, int anything, int64_t* starts
 cru_status cru_ring_emulate(const cru_tensor* q_share, const cru_tensor* k,
                             const cru_tensor* v, int n_chunks, int anything,
                             const int64_t* chunk_sizes, int fused,
-                            const cru_tensor* o, const cru_lse* lse,
+                            int convert_to_fp32, const cru_tensor* o,
+                            const cru_lse* lse,
                             float scale, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
@@ -244,8 +252,8 @@ cru_status cru_usp_workspace_bytes(const cru_tensor* q, int ulysses_degree,
  *   2. for each head group u, the ring over ring_degree equal sequence
  *      chunks: every query row of the group against every chunk, the fp32
  *      partials folded in ascending chunk order (the rows of chunk r are
- *      ring rank r's share; fused selects one split-KV launch per group as
- *      in cru_ring_emulate);
+ *      ring rank r's share; fused and convert_to_fp32 as in
+ *      cru_ring_emulate);
  *   3. head2seq of the group outputs into o.
  *
  *   q, k, v   [B, S, H, D] bf16 or fp32, one sequence (k and v have q's S)
@@ -260,7 +268,8 @@ cru_status cru_usp_workspace_bytes(const cru_tensor* q, int ulysses_degree,
  */
 cru_status cru_usp_emulate(const cru_tensor* q, const cru_tensor* k,
                            const cru_tensor* v, int ulysses_degree,
-                           int ring_degree, int fused, const cru_tensor* o,
+                           int ring_degree, int fused, int convert_to_fp32,
+                           const cru_tensor* o,
                            const cru_lse* lse, float scale, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 

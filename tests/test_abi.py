@@ -140,7 +140,8 @@ def test_merge_validation():
     part = T(dtype=cru.F32)
     assert merge([part], [L()], T(), n=0) == EINVAL
     assert merge([part], [L()], T(), n=cru.MAX_PARTS + 1) == EINVAL
-    assert merge([T()], [L()], T()) == EUNSUPPORTED                    # bf16 partial
+    assert merge([T()], [L()], T()) == EDEVICE                         # bf16 partials pass
+    assert merge([part, T()], [L(), L()], T()) == EUNSUPPORTED         # mixed part dtypes
     assert merge([part, T(S=17, dtype=cru.F32)], [L(), L()], T()) == EINVAL
     odd = T(dtype=cru.F32, strides=(16 * 2 * 64 * 2, 2 * 64, 64))
     assert merge([part, odd], [L(), L()], T()) == EINVAL               # strides differ
@@ -175,11 +176,12 @@ def test_chunk_bounds_divisibility():
         cru.ring_chunk_bounds(4481, 4)               # FLUX 1008x1008 on 4 devices
 
 
-def ring(q, k, v, n, anything=0, sizes=None, fused=0, o=None, ws=FAKE * 4, ws_bytes=1 << 40):
+def ring(q, k, v, n, anything=0, sizes=None, fused=0, o=None, ws=FAKE * 4, ws_bytes=1 << 40,
+         fp32=1):
     o = o or T(S=q.S, D=q.D, dtype=q.dtype)
     arr = None if sizes is None else (ctypes.c_int64 * len(sizes))(*sizes)
     return cru.lib().cru_ring_emulate(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), n,
-                                      anything, arr, fused, ctypes.byref(o), None,
+                                      anything, arr, fused, fp32, ctypes.byref(o), None,
                                       ctypes.c_float(0.0), ws, ws_bytes, None)
 
 
@@ -206,6 +208,10 @@ def test_ring_validation():
     # fp32 inputs take the fp32 path; bf16 output for them is refused
     qf, kf, vf = T(S=10, dtype=cru.F32), T(S=36, dtype=cru.F32), T(S=36, dtype=cru.F32)
     assert ring(qf, kf, vf, 4, o=T(S=10)) == EUNSUPPORTED
+    # bf16 partials (convert_to_fp32 off): bf16 inputs only
+    assert ring(q, k, v, 4, anything=1, fp32=0) == EDEVICE
+    assert ring(qf, kf, vf, 4, fp32=0, o=T(S=10, dtype=cru.F32)) == EUNSUPPORTED
+    assert ring(q, k, v, 4, anything=1, fp32=2) == EINVAL
 
 
 def s2h(xs, P, ys=None, anything=0):
@@ -262,10 +268,10 @@ def test_head_bounds():
     assert cru.ulysses_head_bounds(30, 4, anything=True)[2] == (16, 23)
 
 
-def usp(q, k, v, Pu, Pr, fused=0, o=None, ws=FAKE * 4, ws_bytes=1 << 40):
+def usp(q, k, v, Pu, Pr, fused=0, o=None, ws=FAKE * 4, ws_bytes=1 << 40, fp32=1):
     o = o or T(S=q.S, H=q.H, D=q.D, dtype=q.dtype)
     return cru.lib().cru_usp_emulate(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), Pu, Pr,
-                                     fused, ctypes.byref(o), None, ctypes.c_float(0.0), ws,
+                                     fused, fp32, ctypes.byref(o), None, ctypes.c_float(0.0), ws,
                                      ws_bytes, None)
 
 
@@ -279,6 +285,8 @@ def test_usp_validation():
     assert usp(q, q, q, 0, 2) == EINVAL
     assert usp(q, q, q, 2, 0) == EINVAL
     assert usp(q, q, q, 2, 2, fused=2) == EINVAL
+    assert usp(q, q, q, 2, 2, fp32=0) == EDEVICE
+    assert usp(q, q, q, 2, 2, fp32=5) == EINVAL
     assert usp(q, q, q, 2, 2, ws=0) == EWORKSPACE
     need = ctypes.c_size_t(0)
     assert cru.lib().cru_usp_workspace_bytes(ctypes.byref(q), 2, 2, ctypes.byref(need)) == OK
@@ -305,8 +313,7 @@ def test_config_rules():
     with pytest.raises(ValueError):
         C(ulysses_degree=2, ring_degree=2, ulysses_anything=True)
     C(ulysses_degree=4, ulysses_anything=True)
-    with pytest.raises(NotImplementedError):
-        C(ring_degree=2, convert_to_fp32=False)
+    C(ring_degree=2, convert_to_fp32=False)
 
 
 def test_binding_rejects_bad_tensors_before_the_library():

@@ -223,10 +223,12 @@ def test_identity_v_gives_probabilities(D):
 
 @pytest.mark.parametrize("n", [1, 2, 5, 8, 13, 17, 40])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_merge_kernel(out_dtype, n):
+@pytest.mark.parametrize("part_dtype", [torch.float32, torch.bfloat16])
+def test_merge_kernel(part_dtype, out_dtype, n):
     g = torch.Generator().manual_seed(11 + n)
     shape = (2, 333, 3, 128) if n <= 8 else (1, 77, 2, 64)
-    parts = [torch.randn(shape, generator=g) for _ in range(n)]
+    # the oracle merges exactly the values the GPU reads (bf16 parts upcast)
+    parts = [torch.randn(shape, generator=g).to(part_dtype) for _ in range(n)]
     B, S, H, _ = shape
     lses = [torch.randn(B, H, S, generator=g) * 4 for _ in range(n)]
     lses[n // 2][:, :, :50] = -float("inf")     # one part empty for some rows
@@ -238,6 +240,7 @@ def test_merge_kernel(out_dtype, n):
                               out_dtype=out_dtype)
     torch.cuda.synchronize()
     ref_parts = [p.double().numpy() for p in parts]
+    assert parts[0].dtype == part_dtype
     ref_parts[n // 2] = np.nan_to_num(ref_parts[n // 2])   # the oracle weights them by 0
     o_ref, l_ref = oracle.merge_closed_form(ref_parts, [x.double().numpy() for x in lses])
     tol = TOL_F32 if out_dtype == torch.float32 else TOL_O
@@ -363,6 +366,59 @@ def test_usp_bf16_workloads(idx, Pu, Pr):
     assert err(to_f64(l_s), to_f64(l_full)) <= TOL_PAIR_LSE
     check_rows(o_s, l_s, to_f64(q), to_f64(k), to_f64(v), sample_rows(w.S, 24, seed=Pu * Pr),
                TOL_O, TOL_LSE, f"usp {w.name}")
+
+
+# --------------------------------- partials in the model dtype (bf16)
+
+def tol_bf16_partials(v):
+    """Partial outputs rounded to bf16 (unit roundoff 2^-8) add at most
+    2^-8 * max|O_c| <= 2^-8 * max|V| to the final error: the merge's weights
+    sum to one, and every partial output is a convex combination of V rows."""
+    return TOL_O + 2.0 ** -8 * float(v.abs().max())
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_ring_bf16_partials(fused):
+    w = workload(3)
+    (q, k, v), (qd, kd, vd) = inputs(3)
+    N = w.ring_degree
+    a, b = cru.ring_chunk_bounds(w.S, N)[0]
+    say(f"flux-1024 ring share, bf16 partials, fused={fused}")
+    o16, l16 = cru.ring_emulate(qd[:, a:b], kd, vd, N, fused=fused, convert_to_fp32=False)
+    o32, l32 = cru.ring_emulate(qd[:, a:b], kd, vd, N, fused=fused)
+    torch.cuda.synchronize()
+    tol = tol_bf16_partials(vd)
+    # the LSE does not depend on the partials' dtype
+    assert torch.equal(l16, l32)
+    assert err(to_f64(o16), to_f64(o32)) <= tol + TOL_O
+    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
+    rows = sample_rows(b - a, 32, seed=3)
+    o_ref, l_ref = oracle.attention(q64[:, a:b][:, rows], k64, v64)
+    eo = err(to_f64(o16)[:, rows], o_ref)
+    say(f"  bf16 partials: max|dO| = {eo:.3e} (bound {tol:.3e})")
+    assert eo <= tol
+    assert err(to_f64(l16)[:, :, rows], l_ref) <= TOL_LSE
+
+
+def test_ring_bf16_partials_fused_equals_stepwise_and_anything():
+    (q, k, v), (qd, kd, vd) = inputs(4)
+    w = workload(4)
+    o_s, l_s = cru.ring_emulate(qd, kd, vd, w.ring_degree, anything=True, convert_to_fp32=False)
+    o_f, l_f = cru.ring_emulate(qd, kd, vd, w.ring_degree, anything=True, fused=True,
+                                convert_to_fp32=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s, o_f) and torch.equal(l_s, l_f)
+    check_rows(o_s, l_s, to_f64(q), to_f64(k), to_f64(v), sample_rows(w.S, 24, seed=41),
+               tol_bf16_partials(vd), TOL_LSE, "ring anything, bf16 partials")
+
+
+def test_usp_bf16_partials():
+    w = workload(2)
+    (q, k, v), (qd, kd, vd) = inputs(2)
+    o, l = cru.usp_emulate(qd, kd, vd, 2, 3, fused=True, convert_to_fp32=False)
+    torch.cuda.synchronize()
+    check_rows(o, l, to_f64(q), to_f64(k), to_f64(v), sample_rows(w.S, 24, seed=42),
+               tol_bf16_partials(vd), TOL_LSE, "usp 2 x 3, bf16 partials")
 
 
 # ------------------------------------------------- the five workloads, full size
