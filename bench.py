@@ -51,9 +51,11 @@ def attn_flops(B, H, Sq, Skv, D):
     return 4.0 * B * H * Sq * Skv * D
 
 
-def merge_bytes(n, B, S, H, D, out_bytes=2):
+def merge_bytes(n, B, S, H, D, out_bytes=2, part_bytes=4):
+    """Algorithmic bytes of an n-way merge: every part's O and LSE read once,
+    O and LSE written once."""
     rows = B * S * H
-    return n * (rows * D * 4 + rows * 4) + rows * D * out_bytes + rows * 4
+    return n * (rows * D * part_bytes + rows * 4) + rows * D * out_bytes + rows * 4
 
 
 def source_sha256(path):
@@ -241,7 +243,17 @@ def main():
                   "bytes": mbytes, "ms_median": med, "ms_min": mn,
                   "GB/s": mbytes / (med * 1e-3) / 1e9,
                   "frac_hbm_peak": mbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS}
-    del parts_o, parts_l
+    # the same merge with partials kept in bf16 (convert_to_fp32 off)
+    parts_b = [p_.to(torch.bfloat16) for p_ in parts_o]
+    del parts_o
+    mbytes_b = merge_bytes(N, B, S, H, D, part_bytes=2)
+    medb, mnb = cold(lambda: cru.attn_merge_lse(parts_b, parts_l, out=o_merge, lse=l_merge),
+                     args.cold_reps)
+    cold_merge_bf16 = {"workload": "flux-1024, 8 bf16 partials over all 4608 rows -> bf16 O + LSE",
+                       "bytes": mbytes_b, "ms_median": medb, "ms_min": mnb,
+                       "GB/s": mbytes_b / (medb * 1e-3) / 1e9,
+                       "frac_hbm_peak": mbytes_b / (medb * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    del parts_b, parts_l
 
     wv = workload(5)
     qv, kv_, vv = (t.to(dev) for t in make_inputs(5))
@@ -309,6 +321,24 @@ def main():
     usp_ms = statistics.median(ts)
     usp = {"workload": f"flux-1024, ulysses {Pu} x ring {Pr}, all devices' shares, fused ring",
            "ms_median": usp_ms, "TFLOP/s": f_full / (usp_ms * 1e-3) / 1e12}
+
+    # the step's ring share with partials kept in bf16 (convert_to_fp32 off)
+    run_rb = lambda: cru.ring_emulate(q_share, k, v, N, fused=True, convert_to_fp32=False,
+                                      out=o_ring, lse=l_ring, workspace=ws)
+    for _ in range(3):
+        run_rb()
+    ts = []
+    for _ in range(20):
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        run_rb()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    rb_ms = statistics.median(ts)
+    ring_bf16 = {"workload": "flux-1024 ring rank-0 share (576 rows x 8 chunks), bf16 partials",
+                 "ms_median": rb_ms, "TFLOP/s": f_ring / (rb_ms * 1e-3) / 1e12,
+                 "fp32_partials_ms_in_step": part_ms["ring_share"]}
     del usp_ws, o_usp, l_usp
     torch.cuda.synchronize()
 
@@ -338,6 +368,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "usp": usp,
+        "ring_share_bf16_partials": ring_bf16,
+        "cold_merge_bf16_partials": cold_merge_bf16,
         "ulysses_anything_cold_layout": anything_layout,
         "parts_ms": part_ms,
         "attn_full_tflops": attn_tflops,
