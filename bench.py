@@ -21,6 +21,7 @@ merge and layout kernels, and the fp64 oracle timed on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
     python bench.py --copy-calibration   # plain copy of known size, for counters
+    python bench.py --attn-only N        # N FLUX-1024 forwards only, for counters
 """
 from __future__ import annotations
 
@@ -121,6 +122,21 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}))
 
 
+def attn_only(n):
+    """n full forwards at FLUX-1024 and nothing else, for counter collection."""
+    import torch
+    import context_ring_ulysses_amd as cru
+    from workloads import make_inputs, workload
+    w = workload(3)
+    q, k, v = (t.cuda() for t in make_inputs(3))
+    o = torch.empty_like(q)
+    l = torch.empty(w.B, w.H, w.S, dtype=torch.float32, device=q.device)
+    for _ in range(n):
+        cru.attn_fwd_lse(q, k, v, out=o, lse=l)
+    torch.cuda.synchronize()
+    log(f"[bench] {n} FLUX-1024 forwards done")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +145,8 @@ def main():
     ap.add_argument("--cold-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--attn-only", type=int, default=0, metavar="N",
+                    help="run N FLUX-1024 full forwards and exit (for counter passes)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -142,6 +160,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.attn_only:
+        attn_only(args.attn_only)
         return
 
     dev = torch.device("cuda:0")

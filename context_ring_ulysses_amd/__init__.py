@@ -97,8 +97,7 @@ def lib() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python context_ring_ulysses_amd/build.py` "
-            "(or __graft_entry__.build()) first")
+            f"{LIB_PATH} is not built; run `python context_ring_ulysses_amd/build.py` first")
     L = ctypes.CDLL(LIB_PATH)
     T, Lse = _P(CruTensor), _P(CruLse)
     st = ctypes.c_int
