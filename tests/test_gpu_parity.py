@@ -249,6 +249,92 @@ def test_merge_kernel(part_dtype, out_dtype, n):
     assert torch.isneginf(l[B - 1, H - 1, 7]).item() and (o[B - 1, 7, H - 1] == 0).all().item()
 
 
+# ------------------------------------------- adversarial softmax and long rows
+
+def _ramp_inputs(seed, S, D, slope, B=1, H=2):
+    """Keys along one direction with growing weight, so every query's logits
+    climb along the keys and the running max moves at every tile."""
+    g = torch.Generator().manual_seed(seed)
+    u = torch.randn(D, generator=g)
+    u = u / u.norm()
+    q = (u * math.sqrt(D)).expand(B, S, H, D).clone() + 0.05 * torch.randn(B, S, H, D, generator=g)
+    ramp = torch.linspace(0.0, slope, S).view(1, S, 1, 1)
+    k = ramp * u.view(1, 1, 1, D) + 0.05 * torch.randn(B, S, H, D, generator=g)
+    v = torch.randn(B, S, H, D, generator=g)
+    return tuple(t.to(torch.bfloat16) for t in (q, k, v))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("slope", [20.0, 200.0])
+def test_running_max_moves_every_tile(D, slope):
+    # logits rise by up to slope*sqrt(D)/sqrt(D) = slope over the keys: with
+    # the lazy threshold of 8 (log2 units) the max moves at (nearly) every
+    # 64-key tile, and the last tile's keys dominate
+    q, k, v = _ramp_inputs(7, 517, D, slope)
+    o, l = cru.attn_fwd_lse(*cuda(q, k, v))
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v))
+    eo, el = err(to_f64(o), o_ref), err(to_f64(l), l_ref)
+    say(f"ramp D={D} slope={slope}: max|dO| = {eo:.3e}, max|dLSE| = {el:.3e}, LSE range "
+        f"[{l_ref.min():.1f}, {l_ref.max():.1f}]")
+    assert eo <= TOL_O and el <= TOL_LSE
+
+
+@pytest.mark.parametrize("scale_to", [300.0, -300.0, 1e-4])
+def test_extreme_logit_ranges(scale_to):
+    # all logits near +-300 (exp of the raw value would overflow fp32) or
+    # nearly zero (uniform weights); the max shift must keep P in range
+    g = torch.Generator().manual_seed(13)
+    B, S, H, D = 1, 200, 2, 128
+    q = torch.randn(B, S, H, D, generator=g)
+    k = torch.randn(B, S, H, D, generator=g)
+    v = torch.randn(B, S, H, D, generator=g)
+    q = q / q.norm(dim=-1, keepdim=True)
+    k = k / k.norm(dim=-1, keepdim=True)
+    # s = scale * q.k with |q| = 1, |k| = |scale_to| / scale, k along +-q for half the keys
+    k[:, ::2] = q[:, ::2].sign() * q[:, ::2].abs()
+    k = k * (abs(scale_to) * math.sqrt(D))
+    if scale_to < 0:
+        k = -k
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    o, l = cru.attn_fwd_lse(*cuda(q, k, v))
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all().item() and torch.isfinite(l).all().item()
+    o_ref, l_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v))
+    assert err(to_f64(o), o_ref) <= TOL_O
+    # |s| reaches 300 here: the fp32 sum of D products in the MFMA rounds by
+    # at most D * 2^-24 * max|s|, which the LSE inherits
+    assert err(to_f64(l), l_ref) <= TOL_LSE + D * 2.0 ** -24 * 300.0
+
+
+def test_dominant_last_key_in_ragged_tile():
+    # one key, the last of a ragged final tile, outweighs all others by e^40
+    g = torch.Generator().manual_seed(14)
+    B, S, H, D = 1, 131, 3, 64
+    q = torch.randn(B, 70, H, D, generator=g)
+    k = torch.randn(B, S, H, D, generator=g) * 0.1
+    v = torch.randn(B, S, H, D, generator=g)
+    k[:, S - 1] = q[:, 0] / q[:, 0].norm(dim=-1, keepdim=True) * 40.0 * math.sqrt(D) / \
+        q[:, 0].norm(dim=-1, keepdim=True)
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    o, l = cru.attn_fwd_lse(*cuda(q, k, v))
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v))
+    assert err(to_f64(o), o_ref) <= TOL_O and err(to_f64(l), l_ref) <= TOL_LSE
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_long_sequence_sampled(D):
+    # 40000 keys: index arithmetic well past 2^16 rows, 625 key tiles
+    B, S, H = 1, 40000, 2
+    q, k, v = random_qkv(500 + D, B=B, Sq=S, Skv=S, H=H, D=D, gain=math.sqrt(3.0))
+    say(f"long sequence S={S} D={D}")
+    o, l = cru.attn_fwd_lse(*cuda(q, k, v))
+    torch.cuda.synchronize()
+    check_rows(o, l, to_f64(q), to_f64(k), to_f64(v), sample_rows(S, 12, seed=D),
+               TOL_O, TOL_LSE, f"S={S} D={D}")
+
+
 # -------------------------------------------------------- layouts, bit-exact
 
 @pytest.mark.parametrize("idx", [2, 5])
