@@ -57,14 +57,22 @@
 // with no per-load bounds arithmetic.
 //
 // The running max m is kept in log2 units (scores times scale*log2(e)), so
-// P = 2^(x - m) is one FMA and one v_exp_f32 per score.  Rescaling is lazy:
-// m only moves when some row's tile max passes it by more than kTau, so P
-// may reach 2^kTau (fp32 sums and bf16 P hold that as well as values below
-// 1) and the 64-register rescale of O is rare.  The rescale a move owes is
-// settled at the start of the next tile, ahead of its QK^T block, so its
-// branch never splits the block the compiler interleaves (QK^T, max, P V of
-// the previous tile, exponentials).  The row sum l adds the fp32 P; only the
-// P V product sees P rounded to bf16.
+// P = 2^(x - m) is one FMA and one v_exp_f32 per score.  Rescaling is lazy
+// and the tile max is not computed on the common path: tile t is
+// exponentiated against the current m, and only if some half-row's sum of
+// the tile's P passes 2^kSumCap (which bounds every P of the tile, an
+// overflow to inf included) does the wave take the rare path that finds
+// the tile max, moves m there and exponentiates the tile again.  Any m gives
+// the same O and LSE up to rounding (fp32 and bf16 keep their relative
+// precision at any scale below overflow); the cap only keeps P, l and O far
+// from the fp32 limit.  The first tile sets m to its own max.  The
+// 64-register rescale of O that a move owes is settled at the start of the
+// next tile, ahead of its QK^T block, so its branch never splits the block
+// the compiler interleaves (QK^T, exponentials, P V of the previous tile).
+// P is rounded to bf16 for the P V product, and O is normalised by the sum
+// of those same rounded values, so O's weights sum to one and a row that one
+// key dominates keeps that key's rounding out of O.  The LSE takes the sum
+// of the fp32 P, which the rounding would otherwise bias by up to 2^-9.
 #include "attn_shape.h"
 #include "cru_kernels.h"
 
@@ -80,7 +88,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16;
 
-constexpr float kTau = 8.0f;   // lazy rescale threshold, log2 units
+constexpr float kSumCap = 4294967296.0f;   // 2^32: bound on a half-row's tile sum of P
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
 constexpr int kWaitVmem = 0x0F70;        // s_waitcnt vmcnt(0), other counters not waited
@@ -210,7 +218,8 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
   float m = -__builtin_inff();   // running max of s * scale * log2(e)
-  float l = 0.0f;                // this half-lane's share of the running sum
+  float l = 0.0f;                // this half-lane's share of the running sum of P
+  float lb = 0.0f;               // the same sum over P rounded to bf16 (normalises O)
   // Rescale of O still owed for the last max move (applied just before the
   // next P V product, see the step below).
   float alpha_owed = 1.0f;
@@ -309,62 +318,89 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
     }
 
     f32x16 sc[T::NJ];
-    qk(kb_t, sc);
+    // S^T of tile t; keys past the end of the range (last tile) do not exist
+    auto scores = [&]() {
+      qk(kb_t, sc);
+      if constexpr (kLastTile) {
+        const int valid = nkv - t * T::BC;
+#pragma unroll
+        for (int jb = 0; jb < T::NJ; ++jb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = jb * 32 + 16 * (r >> 3) + 8 * lh + (r & 7);
+            if (key >= valid) sc[jb][r] = -__builtin_inff();
+          }
+      }
+    };
+    scores();
 
-    if constexpr (kLastTile) {
-      // keys past the end of the range do not exist
-      const int valid = nkv - t * T::BC;
+    // P = 2^(s*scale*log2e - m), rounded to bf16 (nearest even) for the
+    // P V product.  lt sums the fp32 P (for the LSE), ltb the bf16 P that
+    // the product sees (for O's normaliser); both are this half-lane's share
+    // of the tile's sum.
+    auto exps = [&](float mref, float& lt, float& ltb) {
+      lt = 0.0f;
+      ltb = 0.0f;
 #pragma unroll
       for (int jb = 0; jb < T::NJ; ++jb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = jb * 32 + 16 * (r >> 3) + 8 * lh + (r & 7);
-          if (key >= valid) sc[jb][r] = -__builtin_inff();
-        }
-    }
-
-    // online softmax: tile max of this row (both halves); the running max
-    // only moves when some row's tile max passes it by more than kTau
-    float mx = sc[0][0];
+        for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-    for (int jb = 0; jb < T::NJ; ++jb)
+          for (int t2 = 0; t2 < 4; ++t2) {
+            const float p0 = __builtin_amdgcn_exp2f(
+                __builtin_fmaf(sc[jb][hf * 8 + 2 * t2], a.scale_log2, -mref));
+            const float p1 = __builtin_amdgcn_exp2f(
+                __builtin_fmaf(sc[jb][hf * 8 + 2 * t2 + 1], a.scale_log2, -mref));
+            lt += p0;
+            lt += p1;
+            const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+            ltb = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, ltb,
+                                                  false);
+            p_new[jb][hf][2 * t2] = pp[0];
+            p_new[jb][hf][2 * t2 + 1] = pp[1];
+          }
+    };
+    // max of this row's scores in the tile (both halves), in log2 units
+    auto tile_max = [&]() {
+      float mx = sc[0][0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[jb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mxs = mx * a.scale_log2;
-    const bool move = __ballot(mxs > m + kTau) != 0ull;
-    const float mn = move ? fmaxf(m, mxs) : m;
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    l *= alpha;
-    m = mn;
+      for (int jb = 0; jb < T::NJ; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[jb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      return mx * a.scale_log2;
+    };
 
-    if constexpr (!kFirst) {
-      // tile t-1, whose P is relative to the max after its move
+    if constexpr (kFirst) {
+      // O and l are empty: start from the tile's own max, nothing is owed
+      m = tile_max();
+      exps(m, l, lb);
+      owed = false;
+    } else {
+      float lt, ltb;
+      exps(m, lt, ltb);
+      // tile t-1, whose P is relative to m before this tile
       pv(vb_p, p_prev);
+      // rare: some P of this tile is too large for the current m
+      const bool move = __ballot(lt > kSumCap) != 0ull;
+      if (move) {
+        // S^T is recomputed from the K tile (still in LDS until the next
+        // barrier) rather than kept live across the P V block
+        asm volatile("" ::: "memory");
+        scores();
+        const float mn = fmaxf(m, tile_max());
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        l *= alpha;
+        lb *= alpha;
+        m = mn;
+        alpha_owed = alpha;
+        exps(m, lt, ltb);
+      }
+      // tiles up to t-1 are now in O relative to m before this tile's move
+      owed = move;
+      l += lt;
+      lb += ltb;
     }
-    // tiles up to t-1 are now in O relative to the max before this tile's
-    // move (tile 0 leaves O empty, so nothing is owed after it)
-    owed = kFirst ? false : move;
-    alpha_owed = alpha;
-
-    // P = 2^(s*scale*log2e - m) <= 2^kTau, summed in fp32 for l (and so for the
-    // LSE) and rounded to bf16 (nearest even) for the P V product
-#pragma unroll
-    for (int jb = 0; jb < T::NJ; ++jb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int t2 = 0; t2 < 4; ++t2) {
-          const float p0 = __builtin_amdgcn_exp2f(
-              __builtin_fmaf(sc[jb][hf * 8 + 2 * t2], a.scale_log2, -m));
-          const float p1 = __builtin_amdgcn_exp2f(
-              __builtin_fmaf(sc[jb][hf * 8 + 2 * t2 + 1], a.scale_log2, -m));
-          l += p0;
-          l += p1;
-          const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
-          p_new[jb][hf][2 * t2] = pp[0];
-          p_new[jb][hf][2 * t2 + 1] = pp[1];
-        }
 
     // this wave's loads must land before the next barrier publishes them
     __builtin_amdgcn_s_waitcnt(kWaitVmem);
@@ -410,9 +446,10 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
     }
   }
 
-  // epilogue: O = O_acc / l, LSE = (m + log2 l) ln 2; no keys -> O = 0, -inf
+  // epilogue: O = O_acc / lb, LSE = (m + log2 l) ln 2; no keys -> O = 0, -inf
   const float lt = l + __shfl_xor(l, 32);
-  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  const float lbt = lb + __shfl_xor(lb, 32);
+  const float inv = lbt > 0.0f ? 1.0f / lbt : 0.0f;
   const float lse = lt > 0.0f ? (m + log2f(lt)) * kLn2 : -__builtin_inff();
   if (row < a.Sq) {
     const int64_t obase = split * a.o_split_stride + b * a.o_sb + (int64_t)row * a.o_ss + h * a.o_sh;
