@@ -88,12 +88,25 @@ def cpu_baseline(budget_s=10.0, max_forwards=480):
     same flop count as the GPU."""
     import oracle
     from workloads import make_inputs, to_f64, workload
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([d.get("num_threads", 1) for d in threadpool_info()
-                     if d.get("user_api") == "blas"] or [1])
+        pools = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        cores = max([d.get("num_threads", 1) for d in pools] or [1])
+        if pools:
+            blas = ", ".join(f"{d.get('internal_api', '?')} {d.get('version', '')}".strip()
+                             for d in pools)
     except Exception:
         cores = os.cpu_count() or 1
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     w = workload(3)
     q, k, v = make_inputs(3)
     done, spent = 0, 0.0
@@ -106,7 +119,8 @@ def cpu_baseline(budget_s=10.0, max_forwards=480):
         done += 1
     flops = attn_flops(1, done, w.S, w.S, w.D)
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model, "blas": blas,
+            "host_cpus_visible": len(os.sched_getaffinity(0)),
             "sample": f"fp64 oracle full forward of FLUX-1024 (S=4608, D=128, all rows), "
                       f"{done} single-head forwards (heads cycled), {spent:.1f} s"}
 
