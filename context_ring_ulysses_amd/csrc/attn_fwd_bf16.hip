@@ -28,7 +28,8 @@
 // 32x32 MFMA gives lane (i, half) the column i -- one query row -- and rows
 // 8*(r/4) + 4*half + r%4 for its 16 registers r.  So every lane owns one
 // query row: the running max, the sum and the O rescale factor are per-lane
-// scalars, and only the two halves of a row need one exchange per tile.
+// scalars, and the two halves of a row meet only in the epilogue and when the
+// running max moves.
 //
 // O^T = V^T P^T then uses A = 32 dims x 16 keys of V^T and B = P^T, which the
 // lane already holds in its S^T registers.  For registers 0..7 (and 8..15)
@@ -60,7 +61,7 @@
 // P = 2^(x - m) is one FMA and one v_exp_f32 per score.  Rescaling is lazy
 // and the tile max is not computed on the common path: tile t is
 // exponentiated against the current m, and only if some half-row's sum of
-// the tile's P passes 2^kSumCap (which bounds every P of the tile, an
+// the tile's P passes kSumCap = 2^32 (the sum bounds every P of the tile, an
 // overflow to inf included) does the wave take the rare path that finds
 // the tile max, moves m there and exponentiates the tile again.  Any m gives
 // the same O and LSE up to rounding (fp32 and bf16 keep their relative
