@@ -342,6 +342,89 @@ def test_long_sequence_sampled(D):
                TOL_O, TOL_LSE, f"S={S} D={D}")
 
 
+# Batch strides past 2^31 elements: every batch offset needs 64-bit address
+# arithmetic in the kernels.  The views sit in 4-9 GB device buffers of which
+# only the used rows are written or read.
+BIG_SB = (1 << 31) + 12288
+
+
+def _big_view(x, dtype, sb=BIG_SB):
+    """A [B, S, H, D] device view of x (CPU) whose batch stride is sb elements."""
+    B, S, H, D = x.shape
+    buf = torch.empty((B - 1) * sb + S * H * D, dtype=dtype, device="cuda")
+    for b in range(B):
+        buf[b * sb: b * sb + S * H * D].copy_(x[b].reshape(-1).to(dtype))
+    return torch.as_strided(buf, (B, S, H, D), (sb, H * D, D, 1))
+
+
+def _big_empty(shape, dtype, sb=BIG_SB):
+    B, S, H, D = shape
+    buf = torch.empty((B - 1) * sb + S * H * D, dtype=dtype, device="cuda")
+    return torch.as_strided(buf, shape, (sb, H * D, D, 1))
+
+
+def _free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_attention_batch_stride_past_2_31(dtype):
+    B, S, H, D = 2, 200, 2, 128
+    q, k, v = random_qkv(41, B=B, Sq=S, Skv=S, H=H, D=D, gain=math.sqrt(3.0),
+                         dtype="bf16" if dtype == torch.bfloat16 else "f32")
+    say(f"attention ({dtype}) with batch strides of {BIG_SB} elements")
+    qd, kd, vd = (_big_view(t, dtype) for t in (q, k, v))
+    o = _big_empty((B, S, H, D), dtype)
+    lbuf = torch.empty((B - 1) * BIG_SB + H * S, dtype=torch.float32, device="cuda")
+    l = torch.as_strided(lbuf, (B, H, S), (BIG_SB, S, 1))
+    cru.attn_fwd_lse(qd, kd, vd, out=o, lse=l)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v))
+    o_h = torch.stack([o[b].cpu() for b in range(B)])
+    l_h = torch.stack([l[b].cpu() for b in range(B)])
+    del qd, kd, vd, o, l, lbuf
+    _free()
+    bf16 = dtype == torch.bfloat16
+    assert err(to_f64(o_h), o_ref) <= (TOL_O if bf16 else TOL_F32)
+    assert err(to_f64(l_h), l_ref) <= (TOL_LSE if bf16 else TOL_F32)
+
+
+def test_merge_batch_stride_past_2_31():
+    B, S, H, D, n = 2, 150, 3, 128, 3
+    g = torch.Generator().manual_seed(42)
+    parts = [torch.randn(B, S, H, D, generator=g) for _ in range(n)]
+    lses = [torch.randn(B, H, S, generator=g) * 4 for _ in range(n)]
+    say(f"merge of {n} fp32 parts with batch strides of {BIG_SB} elements")
+    pd = [_big_view(x, torch.float32) for x in parts]
+    o = _big_empty((B, S, H, D), torch.bfloat16)
+    cru.attn_merge_lse(pd, [x.cuda() for x in lses], out=o)
+    torch.cuda.synchronize()
+    o_h = torch.stack([o[b].cpu() for b in range(B)])
+    del pd, o
+    _free()
+    o_ref, _ = oracle.merge_closed_form([x.double().numpy() for x in parts],
+                                        [x.double().numpy() for x in lses])
+    assert err(to_f64(o_h), o_ref) <= TOL_O
+
+
+def test_layouts_batch_stride_past_2_31():
+    B, S, H, D, P = 2, 96, 6, 64, 3
+    x = torch.randn(B, S, H, D, generator=torch.Generator().manual_seed(43)).to(torch.bfloat16)
+    say(f"seq2head/head2seq with batch strides of {BIG_SB} elements")
+    xd = _big_view(x, torch.bfloat16)
+    y = cru.ulysses_seq2head(xd, P)
+    back = _big_empty((B, S, H, D), torch.bfloat16)
+    cru.ulysses_head2seq(y, P, out=back)
+    torch.cuda.synchronize()
+    y_h = y.cpu()
+    back_h = torch.stack([back[b].cpu() for b in range(B)])
+    del xd, y, back
+    _free()
+    assert np.array_equal(y_h.view(torch.int16).numpy(), oracle.seq2head(x.view(torch.int16).numpy(), P))
+    assert torch.equal(back_h.view(torch.int16), x.view(torch.int16))
+
+
 # -------------------------------------------------------- layouts, bit-exact
 
 @pytest.mark.parametrize("idx", [2, 5])
