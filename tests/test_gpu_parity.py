@@ -46,7 +46,8 @@ def err(a, b):
     b = np.asarray(b, dtype=np.float64)
     assert a.shape == b.shape, (a.shape, b.shape)
     both_ninf = np.isneginf(a) & np.isneginf(b)
-    e = np.where(both_ninf, 0.0, np.abs(a - b))
+    with np.errstate(invalid="ignore"):          # -inf - -inf, masked just below
+        e = np.where(both_ninf, 0.0, np.abs(a - b))
     assert not np.isnan(e).any(), "NaN in comparison"
     return float(e.max()) if e.size else 0.0
 
