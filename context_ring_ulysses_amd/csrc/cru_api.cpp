@@ -38,6 +38,16 @@ cru_status fail(cru_status st, const char* fmt, ...) {
   } while (0)
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
+// Largest tensor a descriptor may describe, in elements.  Every product of
+// sizes formed later (grid sizes, element counts) is bounded by a small
+// multiple of this, so none of them can overflow int64_t.
+constexpr int64_t kMaxElems = (int64_t)1 << 48;
+
+// a * b for non-negative a, b, saturating at INT64_MAX instead of overflowing
+int64_t mul_sat(int64_t a, int64_t b) {
+  if (a == 0 || b == 0) return 0;
+  return a > INT64_MAX / b ? INT64_MAX : a * b;
+}
 
 int elem_bytes(int dtype) { return dtype == CRU_BF16 ? 2 : 4; }
 const char* dtype_name(int dtype) { return dtype == CRU_BF16 ? "bf16" : "fp32"; }
@@ -52,7 +62,10 @@ cru_status check_tensor(const cru_tensor* t, const char* name) {
   if (t->B > kMaxDim || t->S > kMaxDim || t->H > kMaxDim || t->D > kMaxDim)
     return fail(CRU_EINVAL, "%s: size above 2^30", name);
   if (t->sb < 0 || t->ss < 0 || t->sh < 0) return fail(CRU_EINVAL, "%s: negative stride", name);
-  const int64_t numel = t->B * t->S * t->H * t->D;
+  const int64_t numel = mul_sat(mul_sat(mul_sat(t->B, t->S), t->H), t->D);
+  if (numel > kMaxElems)
+    return fail(CRU_EINVAL, "%s: [%lld, %lld, %lld, %lld] is above 2^48 elements", name,
+                (long long)t->B, (long long)t->S, (long long)t->H, (long long)t->D);
   if (numel > 0 && t->data == nullptr) return fail(CRU_EINVAL, "%s: data is NULL", name);
   if (reinterpret_cast<uintptr_t>(t->data) % 16 != 0)
     return fail(CRU_EINVAL, "%s: data is not 16-byte aligned", name);

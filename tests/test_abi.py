@@ -116,6 +116,25 @@ def test_attn_fwd_validation(case, expect):
     assert last_error() != ""
 
 
+def test_sizes_whose_product_overflows_are_rejected():
+    # every size is within 2^30, but their product is far above any tensor
+    # (and above 2^63): refused before any product of sizes is formed
+    huge = dict(B=1 << 30, S=1 << 30, H=1 << 10, D=64, strides=(8, 8, 8))
+    q = T(**huge)
+    assert fwd(q, T(S=24), T(S=24), T()) == EINVAL
+    assert "2^48" in last_error()
+    assert merge([T(dtype=cru.F32, **huge)], [L()], T()) == EINVAL
+    need = ctypes.c_size_t(0)
+    assert cru.lib().cru_ring_workspace_bytes(ctypes.byref(q), 4, ctypes.byref(need)) == EINVAL
+    assert s2h([q], 2) == EINVAL
+    assert h2s([q], 2) == EINVAL
+    # just under the cap is accepted by the size check (these fail later, on
+    # the fake pointer or the per-call index range)
+    ok = T(B=1 << 18, S=1 << 12, H=1 << 12, D=64, strides=(8, 8, 8))
+    assert fwd(ok, T(S=24), T(S=24), T()) == EINVAL
+    assert "2^48" not in last_error()
+
+
 def test_valid_call_reaches_device_check_without_gpu():
     # well-formed arguments pass every host check; the fake pointer is then
     # rejected as not being device memory (or there is no device here)
