@@ -38,6 +38,10 @@
  *    be moved 16 bytes at a time.
  *  - The LSE is fp32 [B, H, S], natural log, described by cru_lse (s stride 1).
  *  - Head dims: D = 64 or 128.
+ *  - Sizes: each of B, S, H, D at most 2^30 and B*S*H*D at most 2^48
+ *    elements; one call's kernel work items (threads, 16-byte vectors) below
+ *    2^31 (split larger calls); for the attention, s strides below 2^22
+ *    elements.  Larger requests fail with CRU_EINVAL.
  *  - All checks run on the host before anything is enqueued.  A failed check
  *    returns a non-zero cru_status, enqueues nothing and leaves a message for
  *    cru_last_error() (thread-local).  The checks follow the three classes of
@@ -104,8 +108,10 @@ typedef struct {
  *   scale  > 0, or 0 for 1/sqrt(D)
  *
  * bf16 inputs run on bf16 matrix cores with fp32 accumulation; P is rounded
- * to bf16 (nearest even) before the P V product and O is rounded to nearest
- * even when o is bf16.  fp32 inputs run in fp32 throughout.
+ * to bf16 (nearest even) before the P V product, O is divided by the sum of
+ * those rounded values (the LSE by the sum of the unrounded ones), and O is
+ * rounded to nearest even when o is bf16.  fp32 inputs run in fp32
+ * throughout.
  * Skv = 0 gives O = 0 and LSE = -inf; Sq = 0 enqueues nothing.
  * o must not overlap q, k or v.
  */
