@@ -212,7 +212,10 @@ def attn_merge_lse(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Te
                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                    out_dtype: torch.dtype = torch.bfloat16, return_lse: bool = True
                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Merge fp32 partial results over disjoint key sets (in ascending order)."""
+    """Merge partial results over disjoint key sets, folded in ascending order.
+
+    The partial outputs are all fp32, or all bf16 (the form ring steps leave
+    without convert_to_fp32); the LSEs are fp32.  The sums are fp32 either way."""
     n = len(o_parts)
     if n == 0 or n != len(lse_parts):
         raise CruInvalid(1, "need one LSE per partial output, at least one")
