@@ -699,14 +699,31 @@ def test_ring_anything_uneven_chunks(fused):
     assert err(to_f64(o_r), to_f64(o_c)[:, a:b]) <= TOL_PAIR_O
 
 
-def test_ring_empty_and_explicit_chunks():
+@pytest.mark.parametrize("fused", [False, True])
+def test_ring_empty_and_explicit_chunks(fused):
     q, k, v = random_qkv(13, 1, 100, 90, 2, 128)
     qd, kd, vd = cuda(q, k, v)
     sizes = [0, 40, 0, 1, 49, 0]
-    o, l = cru.ring_emulate(qd, kd, vd, len(sizes), anything=True, chunk_sizes=sizes)
+    o, l = cru.ring_emulate(qd, kd, vd, len(sizes), anything=True, chunk_sizes=sizes, fused=fused)
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.chunked_attention(to_f64(q), to_f64(k), to_f64(v), len(sizes), sizes)
     assert err(to_f64(o), o_ref) <= TOL_O and err(to_f64(l), l_ref) <= TOL_LSE
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_ring_degenerate_degrees(fused):
+    # a ring of one chunk is plain attention; a ring whose chunks are all
+    # empty has no keys at all (O = 0, LSE = -inf)
+    q, k, v = random_qkv(16, 2, 75, 75, 3, 64)
+    qd, kd, vd = cuda(q, k, v)
+    o, l = cru.ring_emulate(qd, kd, vd, 1, fused=fused)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v))
+    assert err(to_f64(o), o_ref) <= TOL_O and err(to_f64(l), l_ref) <= TOL_LSE
+    o, l = cru.ring_emulate(qd, kd[:, :0], vd[:, :0], 4, anything=True, fused=fused,
+                            out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert (o.cpu() == 0).all() and torch.isneginf(l.cpu()).all()
 
 
 def test_device_errors():
