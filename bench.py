@@ -164,8 +164,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's share on one GPU; runs on more than one GPU "
-              "are not part of this build (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU's share of the work on one GPU and has no "
+              "multi-GPU mode (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch
