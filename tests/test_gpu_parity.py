@@ -91,6 +91,22 @@ def test_fp32_tiny_full():
     assert err(to_f64(l), l_ref) <= TOL_F32
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp32_several_tiles_ragged(D):
+    # exact fp32 path past one tile both ways: 257 query rows (3 row tiles of
+    # 128, the last with one row), 300 keys (10 key tiles of 32, the last
+    # with 12), two batches, k given as a strided view
+    q, k, v = random_qkv(17 + D, 2, 257, 300, 3, D, dtype="f32")
+    kd = torch.empty(2, 300, 5, D).cuda()[:, :, 1:4]
+    kd.copy_(k.cuda())
+    assert not kd.is_contiguous()
+    o, l = cru.attn_fwd_lse(q.cuda(), kd, v.cuda())
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v))
+    assert err(to_f64(o), o_ref) <= TOL_F32
+    assert err(to_f64(l), l_ref) <= TOL_F32
+
+
 @pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("rank", [0, 1, 2, 3])
 def test_fp32_tiny_ring_share(rank, fused):
