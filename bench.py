@@ -331,6 +331,67 @@ def main():
         "head2seq_o": {"bytes": 2 * tbytes, "ms_median": meda2,
                        "GB/s": 2 * tbytes / (meda2 * 1e-3) / 1e9,
                        "frac_hbm_peak": 2 * tbytes / (meda2 * 1e-3) / 1e9 / PEAK_HBM_GBS}}
+
+    def warm(fn, reps=20):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return statistics.median(ts)
+
+    # the other bf16 workloads' attention, timed warm like the step (parity
+    # workloads: reported, not targets)
+    lv = torch.empty(wv.B, wv.H, wv.S, dtype=torch.float32, device=dev)
+    fv = attn_flops(wv.B, wv.H, wv.S, wv.S, wv.D)
+    tv_full = warm(lambda: cru.attn_fwd_lse(qv, kv_, vv, out=ov, lse=lv))
+    ov_u = torch.empty_like(ysv[0][0])
+    lv_u = torch.empty(wv.B, wv.H // Pv, wv.S, dtype=torch.float32, device=dev)
+    tv_u = warm(lambda: cru.attn_fwd_lse(ysv[0][0], ysv[1][0], ysv[2][0], out=ov_u, lse=lv_u))
+    w2 = workload(2)
+    q2, k2, v2 = (t.to(dev) for t in make_inputs(2))
+    P2 = w2.ulysses_degree
+    o2 = torch.empty_like(q2)
+    l2 = torch.empty(w2.B, w2.H, w2.S, dtype=torch.float32, device=dev)
+    f2 = attn_flops(w2.B, w2.H, w2.S, w2.S, w2.D)
+    t2_full = warm(lambda: cru.attn_fwd_lse(q2, k2, v2, out=o2, lse=l2))
+    ys2 = [torch.empty(P2, w2.B, w2.S, w2.H // P2, w2.D, dtype=q2.dtype, device=dev)
+           for _ in range(3)]
+    og2 = torch.zeros(P2, w2.B, w2.S, w2.H // P2, w2.D, dtype=q2.dtype, device=dev)
+    lu2 = torch.empty(w2.B, w2.H // P2, w2.S, dtype=torch.float32, device=dev)
+
+    def uly2():
+        cru.ulysses_seq2head([q2, k2, v2], P2, out=ys2)
+        cru.attn_fwd_lse(ys2[0][0], ys2[1][0], ys2[2][0], out=og2[0], lse=lu2)
+        cru.ulysses_head2seq(og2, P2, out=o2)
+
+    t2_u = warm(uly2)
+    t2b = q2.numel() * q2.element_size()
+    m2s, _ = cold(lambda: cru.ulysses_seq2head([q2, k2, v2], P2, out=ys2), args.cold_reps)
+    m2h, _ = cold(lambda: cru.ulysses_head2seq(og2, P2, out=o2), args.cold_reps)
+    other = {
+        "flux-512": {
+            "workload": "flux-512 (B=1, S=1536, H=24, D=128, bf16)",
+            "full_forward": {"ms_median": t2_full, "TFLOP/s": f2 / (t2_full * 1e-3) / 1e12},
+            "ulysses_share_incl_layouts": {"P": P2, "ms_median": t2_u,
+                                           "TFLOP/s": f2 / P2 / (t2_u * 1e-3) / 1e12},
+            "cold_layouts": {"note": "9.4 MB per tensor: launch-bound, and cache-resident "
+                                     "in a real step",
+                             "seq2head_qkv_GB/s": 6 * t2b / (m2s * 1e-3) / 1e9,
+                             "head2seq_o_GB/s": 2 * t2b / (m2h * 1e-3) / 1e9}},
+        "video-dit-4276": {
+            "workload": "video-dit-4276 (B=2, S=4276, H=30, D=64, bf16)",
+            "full_forward": {"ms_median": tv_full, "TFLOP/s": fv / (tv_full * 1e-3) / 1e12},
+            "ulysses_share_attention": {"P": Pv, "ms_median": tv_u,
+                                        "TFLOP/s": fv / Pv / (tv_u * 1e-3) / 1e12}}}
+    log(f"[bench] flux-512 full {other['flux-512']['full_forward']['TFLOP/s']:.0f} TFLOP/s; "
+        f"video full {other['video-dit-4276']['full_forward']['TFLOP/s']:.0f} TFLOP/s")
+    del q2, k2, v2, o2, ys2, og2, lu2, l2, lv, ov_u, lv_u
     del qv, kv_, vv, ysv, ov, ysa, scrub, sink
     torch.cuda.synchronize()
 
@@ -405,6 +466,7 @@ def main():
         "usp": usp,
         "ring_share_bf16_partials": ring_bf16,
         "cold_merge_bf16_partials": cold_merge_bf16,
+        "other_workloads": other,
         "ulysses_anything_cold_layout": anything_layout,
         "parts_ms": part_ms,
         "attn_full_tflops": attn_tflops,
