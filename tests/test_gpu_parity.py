@@ -742,6 +742,59 @@ def test_ring_degenerate_degrees(fused):
     assert (o.cpu() == 0).all() and torch.isneginf(l.cpu()).all()
 
 
+def test_graph_capture_replays_match_eager():
+    # every entry point only enqueues kernels (no allocation, memset or
+    # synchronisation), so a sequence of calls can be captured in a graph.
+    # Each replay, with eager work in between, must equal the eager result
+    # bit for bit.
+    q, k, v = (t.cuda() for t in random_qkv(18, 1, 600, 600, 4, 128, gain=1.7))
+    a, b = cru.ring_chunk_bounds(600, 4)[1]
+    qs = q[:, a:b]
+    ws = torch.empty(cru.ring_workspace_bytes(qs, 4), dtype=torch.uint8, device="cuda")
+    uws = torch.empty(cru.usp_workspace_bytes(q, 2, 3), dtype=torch.uint8, device="cuda")
+    outs = {
+        "o": torch.empty_like(q), "l": torch.empty(1, 4, 600, device="cuda"),
+        "or": torch.empty_like(qs), "lr": torch.empty(1, 4, b - a, device="cuda"),
+        "om": torch.empty_like(q), "lm": torch.empty(1, 4, 600, device="cuda"),
+        "y": torch.empty(2, 1, 600, 2, 128, dtype=q.dtype, device="cuda"),
+        "x": torch.empty_like(q),
+        "ou": torch.empty_like(q), "lu": torch.empty(1, 4, 600, device="cuda"),
+    }
+    parts_o = [torch.randn(1, 600, 4, 128, device="cuda") for _ in range(3)]
+    parts_l = [torch.randn(1, 4, 600, device="cuda") for _ in range(3)]
+
+    def run():
+        cru.attn_fwd_lse(q, k, v, out=outs["o"], lse=outs["l"])
+        cru.ring_emulate(qs, k, v, 4, fused=True, out=outs["or"], lse=outs["lr"], workspace=ws)
+        cru.attn_merge_lse(parts_o, parts_l, out=outs["om"], lse=outs["lm"])
+        cru.ulysses_seq2head(q, 2, out=outs["y"])
+        cru.ulysses_head2seq(outs["y"], 2, out=outs["x"])
+        cru.usp_emulate(q, k, v, 2, 3, fused=True, out=outs["ou"], lse=outs["lu"], workspace=uws)
+
+    run()
+    torch.cuda.synchronize()
+    ref = {n: t.clone() for n, t in outs.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in outs.values():
+            t.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n, t in outs.items():
+            assert torch.equal(t, ref[n]), (rep, n)
+    assert torch.equal(ref["x"], q)
+
+
 def test_device_errors():
     q, k, v = random_qkv(14, 1, 16, 16, 2, 64)
     with pytest.raises(cru.CruDeviceError):
