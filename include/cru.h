@@ -52,6 +52,8 @@
  *  - CRU_EHIP reports a HIP error raised while enqueueing.
  *  - Calls that overlap on one stream are ordered by the stream; concurrent
  *    calls on different streams must not write the same memory.
+ *  - Calls only enqueue kernels (no allocation, memset or synchronisation),
+ *    so they may be captured into a HIP graph and replayed.
  */
 #ifndef CRU_H
 #define CRU_H
