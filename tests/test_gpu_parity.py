@@ -742,6 +742,54 @@ def test_ring_degenerate_degrees(fused):
     assert (o.cpu() == 0).all() and torch.isneginf(l.cpu()).all()
 
 
+def test_random_shape_sweep():
+    # seeded random shapes, each checked against the oracle: attention (bf16,
+    # both head dims, any row and key counts including 1 and ragged tails),
+    # the layouts (bit-exact, even and uneven head groups, both dtypes) and
+    # the merge (random part counts)
+    rng = np.random.default_rng(2024)
+    for case in range(12):
+        B = int(rng.integers(1, 3))
+        H = int(rng.integers(1, 6))
+        D = int(rng.choice([64, 128]))
+        Sq = int(rng.integers(1, 400))
+        Skv = int(rng.integers(1, 400))
+        say(f"sweep {case}: attention B={B} Sq={Sq} Skv={Skv} H={H} D={D}")
+        q, k, v = random_qkv(100 + case, B, Sq, Skv, H, D, gain=float(rng.uniform(0.5, 2.0)))
+        o, l = cru.attn_fwd_lse(*cuda(q, k, v))
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v))
+        assert err(to_f64(o), o_ref) <= TOL_O, case
+        assert err(to_f64(l), l_ref) <= TOL_LSE, case
+
+        P = int(rng.integers(1, 6))
+        anything = H % P != 0 or Skv % P != 0 or bool(rng.integers(0, 2))
+        dtype = torch.bfloat16 if rng.integers(0, 2) else torch.float32
+        say(f"sweep {case}: layouts B={B} S={Skv} H={H} D={D} P={P} anything={anything} {dtype}")
+        x = torch.randn(B, Skv, H, D, generator=torch.Generator().manual_seed(case)).to(dtype)
+        y = cru.ulysses_seq2head(x.cuda(), P, anything=anything)
+        back = cru.ulysses_head2seq(y, P, anything=anything, shape=x.shape)
+        torch.cuda.synchronize()
+        ints = torch.int16 if dtype == torch.bfloat16 else torch.int32
+        groups = cru.ulysses_groups(y, B, Skv, H, D, P)
+        ref = oracle.head_groups(x.view(ints).numpy(), P)
+        assert all(np.array_equal(gr.cpu().view(ints).numpy(), r) for gr, r in zip(groups, ref)), case
+        assert torch.equal(back.cpu().view(ints), x.view(ints)), case
+
+        n = int(rng.integers(1, 20))
+        say(f"sweep {case}: merge of {n} parts")
+        parts = [torch.randn(B, Sq, H, D, generator=torch.Generator().manual_seed(1000 * case + c))
+                 for c in range(n)]
+        lses = [torch.randn(B, H, Sq, generator=torch.Generator().manual_seed(2000 * case + c)) * 3
+                for c in range(n)]
+        om, lm = cru.attn_merge_lse([t.cuda() for t in parts], [t.cuda() for t in lses],
+                                    out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.merge_closed_form([t.double().numpy() for t in parts],
+                                                [t.double().numpy() for t in lses])
+        assert err(to_f64(om), o_ref) <= TOL_F32 and err(to_f64(lm), l_ref) <= TOL_F32, case
+
+
 def test_graph_capture_replays_match_eager():
     # every entry point only enqueues kernels (no allocation, memset or
     # synchronisation), so a sequence of calls can be captured in a graph.
