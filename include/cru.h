@@ -111,11 +111,14 @@ typedef struct {
  *
  * bf16 inputs run on bf16 matrix cores with fp32 accumulation; P is rounded
  * to bf16 (nearest even) before the P V product, O is divided by the sum of
- * those rounded values (the LSE by the sum of the unrounded ones), and O is
- * rounded to nearest even when o is bf16.  fp32 inputs run in fp32
- * throughout.
+ * those rounded values (the LSE is taken from the sum of the unrounded
+ * ones), and O is rounded to nearest even when o is bf16.  fp32 inputs run
+ * in fp32 throughout.
  * Skv = 0 gives O = 0 and LSE = -inf; Sq = 0 enqueues nothing.
  * o must not overlap q, k or v.
+ * Defined by: diffusers "Attention backends" page, "Available backends"
+ * (scaled_dot_product_attention as the default backend); the LSE output:
+ * "Parallelism" API page, ContextParallelConfig.convert_to_fp32.
  */
 cru_status cru_attn_fwd_lse(const cru_tensor* q, const cru_tensor* k,
                             const cru_tensor* v, const cru_tensor* o,
@@ -138,6 +141,11 @@ cru_status cru_attn_fwd_lse(const cru_tensor* q, const cru_tensor* k,
  *   lse        [B, H, S] fp32, or NULL
  *   1 <= n <= CRU_MAX_PARTS
  * Outputs must not overlap the inputs.
+ * Defined by: diffusers "Parallelism" API page, ContextParallelConfig
+ * (convert_to_fp32: each step's output and LSE) and the "Context
+ * parallelism" guide, "Ring Attention" section (one K/V block after
+ * another); the closed form is the identity exp(LSE_c - LSE) exp(s - LSE_c)
+ * = exp(s - LSE).
  */
 cru_status cru_attn_merge_lse(int n, const cru_tensor* o_parts,
                               const cru_lse* lse_parts, const cru_tensor* o,
@@ -160,6 +168,8 @@ cru_status cru_ring_workspace_bytes(const cru_tensor* q_share, int n_chunks,
  * n (CRU_ENOTDIV otherwise), as plain ring attention requires.  Host-only;
  * starts is a host array of n + 1 entries.  Ring rank r's query share is
  * chunk r of the same split.
+ * Defined by: diffusers "Context parallelism" guide, "Ring Anything
+ * Attention" section (sequence lengths that do not divide by the degree).
  */
 cru_status cru_ring_chunk_bounds(int64_t S, int n, int anything, int64_t* starts);
 
@@ -189,6 +199,9 @@ cru_status cru_ring_chunk_bounds(int64_t S, int n, int anything, int64_t* starts
  *   workspace    device memory of at least cru_ring_workspace_bytes(),
  *                256-byte aligned, not overlapping any argument
  * Empty chunks are allowed with anything = 1 and contribute nothing.
+ * Defined by: diffusers "Context parallelism" guide, "Ring Attention" and
+ * "Ring Anything Attention" sections; "Parallelism" API page,
+ * ContextParallelConfig (ring_degree, rotate_method, convert_to_fp32).
  */
 cru_status cru_ring_emulate(const cru_tensor* q_share, const cru_tensor* k,
                             const cru_tensor* v, int n_chunks, int anything,
@@ -204,6 +217,8 @@ cru_status cru_ring_emulate(const cru_tensor* q_share, const cru_tensor* k,
  * more (sizes differ by at most one).  With anything = 0, H must be
  * divisible by P (CRU_ENOTDIV otherwise).  Host-only; starts is a host array
  * of P + 1 entries.
+ * Defined by: diffusers "Context parallelism" guide, "Ulysses Anything
+ * Attention" section (head counts that do not divide by the degree).
  */
 cru_status cru_ulysses_head_bounds(int64_t H, int P, int anything, int64_t* starts);
 
@@ -226,6 +241,8 @@ cru_status cru_ulysses_head_bounds(int64_t H, int P, int anything, int64_t* star
  *                cru_ulysses_head_bounds and lie back to back: group p is a
  *                contiguous [B, S, Hp_p, D] block at element B*S*D*starts[p]
  *                (which is the [P, B, S, Hp, D] layout when P divides H).
+ * Defined by: diffusers "Context parallelism" guide, "Ulysses Attention"
+ * section (the first all-to-all) and "Ulysses Anything Attention" section.
  */
 cru_status cru_ulysses_seq2head(int n, const cru_tensor* x, void* const* y,
                                 int P, int anything, hipStream_t stream);
@@ -239,6 +256,8 @@ cru_status cru_ulysses_seq2head(int n, const cru_tensor* x, void* const* y,
  *       cru_ulysses_seq2head writes them
  *   x   host array of n output views [B, S, H, D] (shape, dtype, strides)
  *   same rules as cru_ulysses_seq2head.
+ * Defined by: the same sections (the second all-to-all regroups the results
+ * by token).
  */
 cru_status cru_ulysses_head2seq(int n, const void* const* y,
                                 const cru_tensor* x, int P, int anything,
@@ -273,6 +292,8 @@ cru_status cru_usp_workspace_bytes(const cru_tensor* q, int ulysses_degree,
  *   scale     as for cru_attn_fwd_lse
  *   workspace device memory of at least cru_usp_workspace_bytes(), 256-byte
  *             aligned, not overlapping any argument
+ * Defined by: diffusers "Context parallelism" guide, "Unified Attention"
+ * section.
  */
 cru_status cru_usp_emulate(const cru_tensor* q, const cru_tensor* k,
                            const cru_tensor* v, int ulysses_degree,
