@@ -147,13 +147,16 @@ __device__ __forceinline__ v4i16 lds_read_tr(const char* base, int byte_off) {
       (__attribute__((address_space(3))) v4i16*)(base + byte_off));
 }
 
+template <int D>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const u16* base, int64_t row0,
                                                            int64_t row_stride, int nrows, int cap) {
-  // rows [row0, row0 + min(nrows, cap)) of a strided [rows, D] bf16 matrix;
-  // the host guarantees cap * row_stride * 2 < 2^31
+  // rows [row0, row0 + min(nrows, cap)) of a strided [rows, D] bf16 matrix:
+  // the range ends with the last element of the last row, so a stride below
+  // D (rows that overlap, or a stride-0 broadcast) still reads every row; the
+  // host guarantees cap * row_stride * 2 < 2^31
   const u16* p = base + row0 * row_stride;
   const int n = nrows < cap ? nrows : cap;
-  const int bytes = n > 0 ? (int)(n * row_stride * 2) : 0;
+  const int bytes = n > 0 ? (int)(((n - 1) * row_stride + D) * 2) : 0;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<u16*>(p), (short)0, bytes, kRsrcWord3);
 }
 
@@ -206,7 +209,7 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
   bf16x8 qf[T::NK];
   {
     const __amdgpu_buffer_rsrc_t qr =
-        rows_rsrc(qg, (int64_t)qt * T::BM, a.q_ss, a.Sq - qt * T::BM, T::BM);
+        rows_rsrc<D>(qg, (int64_t)qt * T::BM, a.q_ss, a.Sq - qt * T::BM, T::BM);
     const int qoff = ((wave * 32 + li) * (int)a.q_ss + lh * 8) * 2;
 #pragma unroll
     for (int ks = 0; ks < T::NK; ++ks)
@@ -220,7 +223,19 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
   float m = -__builtin_inff();   // running max of s * scale * log2(e)
   float l = 0.0f;                // this half-lane's share of the running sum of P
-  float lb = 0.0f;               // the same sum over P rounded to bf16 (normalises O)
+  // Sum of the P rounded to bf16 (O's normaliser), accumulated by the matrix
+  // cores beside O: a 16x16x32 product of a 0/1 pattern with the P^T
+  // registers leaves every lane its own row's sum in all four registers.
+  f32x4 lbacc = {0.0f, 0.0f, 0.0f, 0.0f};
+  // The pattern: lane (row mm = lane%16, k block kk = lane/16) of the A
+  // operand is 1 where (mm/4) and kk have the same parity.  Lane l of a
+  // P^T register holds query l%32 and k block l/16 carries queries n and
+  // n+16 alternately, so output row 4*(l/16)+r of column l%16 sums exactly
+  // the keys of query l%32 (the lane's own row).
+  const bf16x8 ones_pat = [&] {
+    const __bf16 x = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? (__bf16)1.0f : (__bf16)0.0f;
+    return bf16x8{x, x, x, x, x, x, x, x};
+  }();
   // Rescale of O still owed for the last max move (applied just before the
   // next P V product, see the step below).
   float alpha_owed = 1.0f;
@@ -254,7 +269,7 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
   }
 
   auto dma = [&](char* dst, const u16* src, int64_t stride, int t, const int (&off)[T::NLOAD]) {
-    const __amdgpu_buffer_rsrc_t r = rows_rsrc(src, (int64_t)t * T::BC, stride, nkv - t * T::BC, T::BC);
+    const __amdgpu_buffer_rsrc_t r = rows_rsrc<D>(src, (int64_t)t * T::BC, stride, nkv - t * T::BC, T::BC);
 #pragma unroll
     for (int it = 0; it < T::NLOAD; ++it)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + (it * kWaves + wave) * 1024), 16,
@@ -289,6 +304,8 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
           const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr(vb, kb0 + 4 * T::RB + vread[db]));
           const bf16x8 va = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[jb][hf], oacc[db], 0, 0, 0);
+          if (db == T::ND - 1)
+            lbacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_pat, pf[jb][hf], lbacc, 0, 0, 0);
         }
   };
 
@@ -315,6 +332,7 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
         for (int db = 0; db < T::ND; ++db)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha_owed;
+        lbacc *= alpha_owed;
       }
     }
 
@@ -336,12 +354,11 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
     scores();
 
     // P = 2^(s*scale*log2e - m), rounded to bf16 (nearest even) for the
-    // P V product.  lt sums the fp32 P (for the LSE), ltb the bf16 P that
-    // the product sees (for O's normaliser); both are this half-lane's share
+    // P V product (whose row sum the matrix cores take beside it, for O's
+    // normaliser).  lt sums the fp32 P for the LSE: this half-lane's share
     // of the tile's sum.
-    auto exps = [&](float mref, float& lt, float& ltb) {
+    auto exps = [&](float mref, float& lt) {
       lt = 0.0f;
-      ltb = 0.0f;
 #pragma unroll
       for (int jb = 0; jb < T::NJ; ++jb)
 #pragma unroll
@@ -355,8 +372,6 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
             lt += p0;
             lt += p1;
             const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
-            ltb = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, ltb,
-                                                  false);
             p_new[jb][hf][2 * t2] = pp[0];
             p_new[jb][hf][2 * t2 + 1] = pp[1];
           }
@@ -375,32 +390,36 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
     if constexpr (kFirst) {
       // O and l are empty: start from the tile's own max, nothing is owed
       m = tile_max();
-      exps(m, l, lb);
+      exps(m, l);
       owed = false;
     } else {
-      float lt, ltb;
-      exps(m, lt, ltb);
+      float lt;
+      exps(m, lt);
       // tile t-1, whose P is relative to m before this tile
       pv(vb_p, p_prev);
-      // rare: some P of this tile is too large for the current m
-      const bool move = __ballot(lt > kSumCap) != 0ull;
+      // rare: the running sum with this tile's P passes the cap (a P of
+      // this tile overflowing to inf included)
+      const bool move = __ballot(l + lt > kSumCap) != 0ull;
       if (move) {
         // S^T is recomputed from the K tile (still in LDS until the next
         // barrier) rather than kept live across the P V block
         asm volatile("" ::: "memory");
         scores();
-        const float mn = fmaxf(m, tile_max());
+        // the new max covers this tile's scores and, through log2 of the
+        // row's running sum (the LSE so far, in log2 units, which is at
+        // least the max of every earlier score), the earlier tiles: every P
+        // relative to it is at most 1
+        const float lrow = l + __shfl_xor(l, 32);
+        const float mn = fmaxf(fmaxf(m, tile_max()), m + __builtin_amdgcn_logf(lrow));
         const float alpha = __builtin_amdgcn_exp2f(m - mn);
         l *= alpha;
-        lb *= alpha;
         m = mn;
         alpha_owed = alpha;
-        exps(m, lt, ltb);
+        exps(m, lt);
       }
       // tiles up to t-1 are now in O relative to m before this tile's move
       owed = move;
       l += lt;
-      lb += ltb;
     }
 
     // this wave's loads must land before the next barrier publishes them
@@ -413,6 +432,7 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
       for (int db = 0; db < T::ND; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha_owed;
+      lbacc *= alpha_owed;
     }
   };
 
@@ -449,7 +469,7 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
 
   // epilogue: O = O_acc / lb, LSE = (m + log2 l) ln 2; no keys -> O = 0, -inf
   const float lt = l + __shfl_xor(l, 32);
-  const float lbt = lb + __shfl_xor(lb, 32);
+  const float lbt = lbacc[0];   // the whole row's sum (both halves)
   const float inv = lbt > 0.0f ? 1.0f / lbt : 0.0f;
   const float lse = lt > 0.0f ? (m + log2f(lt)) * kLn2 : -__builtin_inff();
   if (row < a.Sq) {

@@ -76,6 +76,49 @@ cru_status check_tensor(const cru_tensor* t, const char* name) {
   return CRU_OK;
 }
 
+// True when the map from indices to element offsets is one to one: with the
+// dims of size > 1 sorted by stride, every stride exceeds the largest offset
+// the smaller-stride dims reach.  (Sufficient, and exact for the layouts
+// strided views of one buffer produce.)
+bool strides_injective(int n, const int64_t* size, const int64_t* stride) {
+  int64_t sz[4], st[4];
+  int m = 0;
+  for (int i = 0; i < n; ++i)
+    if (size[i] == 0) return true;   // no elements
+  for (int i = 0; i < n; ++i)
+    if (size[i] > 1) {
+      sz[m] = size[i];
+      st[m] = stride[i];
+      ++m;
+    }
+  for (int i = 1; i < m; ++i)   // insertion sort by stride
+    for (int j = i; j > 0 && st[j] < st[j - 1]; --j) {
+      const int64_t a = st[j], b = sz[j];
+      st[j] = st[j - 1]; sz[j] = sz[j - 1];
+      st[j - 1] = a; sz[j - 1] = b;
+    }
+  int64_t reach = 0;   // largest offset of the dims taken so far
+  for (int i = 0; i < m; ++i) {
+    if (st[i] <= reach) return false;
+    reach = reach + mul_sat(sz[i] - 1, st[i]);
+    if (reach < 0) return false;
+  }
+  return true;
+}
+
+// An output view: each element must have its own address, or concurrent
+// threads would race on one location (inputs may repeat elements, e.g. a
+// stride-0 broadcast along the sequence).
+cru_status check_output_tensor(const cru_tensor* t, const char* name) {
+  CRU_TRY(check_tensor(t, name));
+  const int64_t size[4] = {t->B, t->S, t->H, t->D};
+  const int64_t stride[4] = {t->sb, t->ss, t->sh, 1};
+  if (!strides_injective(4, size, stride))
+    return fail(CRU_EINVAL, "%s: output strides (%lld, %lld, %lld, 1) make elements overlap", name,
+                (long long)t->sb, (long long)t->ss, (long long)t->sh);
+  return CRU_OK;
+}
+
 cru_status check_head_dim(const cru_tensor* t, const char* name) {
   if (t->D != 64 && t->D != 128)
     return fail(CRU_EUNSUPPORTED, "%s: head dim %lld (supported: 64, 128)", name, (long long)t->D);
@@ -92,6 +135,11 @@ cru_status check_lse(const cru_lse* l, const char* name, int64_t B, int64_t H, i
   if (B * H * S > 0 && l->data == nullptr) return fail(CRU_EINVAL, "%s: data is NULL", name);
   if (reinterpret_cast<uintptr_t>(l->data) % 4 != 0)
     return fail(CRU_EINVAL, "%s: data is not 4-byte aligned", name);
+  const int64_t size[3] = {B, H, S};
+  const int64_t stride[3] = {l->sb, l->sh, 1};
+  if (!strides_injective(3, size, stride))
+    return fail(CRU_EINVAL, "%s: strides (%lld, %lld, 1) make elements overlap", name,
+                (long long)l->sb, (long long)l->sh);
   return CRU_OK;
 }
 
@@ -164,7 +212,7 @@ cru_status check_qkvo(const cru_tensor* q, const cru_tensor* k, const cru_tensor
   CRU_TRY(check_tensor(q, "q"));
   CRU_TRY(check_tensor(k, "k"));
   CRU_TRY(check_tensor(v, "v"));
-  CRU_TRY(check_tensor(o, "o"));
+  CRU_TRY(check_output_tensor(o, "o"));
   if (k->dtype != q->dtype || v->dtype != q->dtype)
     return fail(CRU_EUNSUPPORTED, "q, k, v dtypes differ (%s, %s, %s)", dtype_name(q->dtype),
                 dtype_name(k->dtype), dtype_name(v->dtype));
@@ -282,7 +330,7 @@ cru_status cru_attn_merge_lse(int n, const cru_tensor* o_parts, const cru_lse* l
       return fail(CRU_EINVAL, "lse_parts[%d] strides differ from lse_parts[0]", c);
   }
   CRU_TRY(check_head_dim(p0, "o_parts[0]"));
-  CRU_TRY(check_tensor(o, "o"));
+  CRU_TRY(check_output_tensor(o, "o"));
   if (!same_shape(o, p0)) return fail(CRU_EINVAL, "o shape differs from the parts");
   if (lse != nullptr) CRU_TRY(check_lse(lse, "lse", p0->B, p0->H, p0->S));
   CRU_TRY(check_merge_grid(p0));
@@ -371,6 +419,10 @@ cru_status cru_ring_emulate(const cru_tensor* q_share, const cru_tensor* k, cons
   } else {
     for (int c = 0; c < n_chunks; ++c) {
       if (chunk_sizes[c] < 0) return fail(CRU_EINVAL, "chunk_sizes[%d] < 0", c);
+      // checked before the add, so the running sum stays in [0, Skv]
+      if (chunk_sizes[c] > Skv - start[c])
+        return fail(CRU_EINVAL, "chunk sizes pass the %lld K/V rows at chunk %d", (long long)Skv,
+                    c);
       start[c + 1] = start[c] + chunk_sizes[c];
     }
     if (start[n_chunks] != Skv)
@@ -540,6 +592,7 @@ cru_status cru_ulysses_head2seq(int n, const void* const* y, const cru_tensor* x
     if (reinterpret_cast<uintptr_t>(y[t]) % 16 != 0)
       return fail(CRU_EINVAL, "head2seq: y[%d] is not 16-byte aligned", t);
   }
+  for (int t = 0; t < n; ++t) CRU_TRY(check_output_tensor(&x[t], "x[t]"));
   if (empty) return CRU_OK;
   for (int t = 0; t < n; ++t) {
     CRU_TRY(check_device(y[t], "y[t]"));

@@ -36,6 +36,13 @@
  *    non-negative; the data pointer must be 16-byte aligned and the b/s/h
  *    strides multiples of 8 elements (bf16) or 4 elements (fp32), so rows can
  *    be moved 16 bytes at a time.
+ *  - Input views may repeat elements: a stride of 0 (a broadcast, as torch's
+ *    expand() gives) or rows that overlap (a sequence stride below D) read
+ *    the same values the view describes.  Output views (and output LSEs)
+ *    must give every element its own address: with the dims of size > 1
+ *    sorted by stride, each stride must exceed the largest offset the
+ *    smaller-stride dims reach; other output views fail with CRU_EINVAL.
+ *    Outputs must not share memory with inputs (not checked).
  *  - The LSE is fp32 [B, H, S], natural log, described by cru_lse (s stride 1).
  *  - Head dims: D = 64 or 128.
  *  - Sizes: each of B, S, H, D at most 2^30 and B*S*H*D at most 2^48
@@ -156,6 +163,9 @@ cru_status cru_attn_merge_lse(int n, const cru_tensor* o_parts,
  * needs for a query share shaped like q_share cut into n_chunks chunks
  * (n_chunks fp32 partial outputs and LSEs).  The same size serves both the
  * step-wise and the fused schedule, and bf16 partials (which use less).
+ * The partials are the per-step output and LSE that ring attention carries
+ * in fp32: diffusers "Parallelism" API page, ContextParallelConfig,
+ * convert_to_fp32.  Host-only; bytes is written on success.
  */
 cru_status cru_ring_workspace_bytes(const cru_tensor* q_share, int n_chunks,
                                     size_t* bytes);
@@ -186,7 +196,9 @@ cru_status cru_ring_chunk_bounds(int64_t S, int n, int anything, int64_t* starts
  *                1: any Skv ("Ring Anything": chunks may differ in length)
  *   chunk_sizes  host array of n_chunks lengths summing to Skv, or NULL for
  *                the near-equal split (the first Skv mod n chunks get one
- *                extra row); with anything = 0 they must all be equal
+ *                extra row); with anything = 0 they must all be equal.  Each
+ *                is checked against the rows left before it is added
+ *                (CRU_EINVAL), so no sum can wrap around
  *   fused        0: one attention launch per chunk (the ring's step order);
  *                1: one launch over every (chunk, query tile, head)
  *   convert_to_fp32  1: fp32 partial outputs (ContextParallelConfig's
@@ -266,7 +278,11 @@ cru_status cru_ulysses_head2seq(int n, const void* const* y,
 /*
  * cru_usp_workspace_bytes -- bytes of device workspace cru_usp_emulate needs
  * for q's shape and the two degrees (the same size serves bf16 and fp32
- * outputs).  Same divisibility rules as cru_usp_emulate.
+ * outputs).  Same divisibility rules as cru_usp_emulate.  It holds the
+ * regrouped q, k, v and output of the Ulysses all-to-all (diffusers "Context
+ * parallelism" guide, "Unified Attention" section) and one ring workspace of
+ * fp32 partials (diffusers "Parallelism" API page, ContextParallelConfig,
+ * convert_to_fp32).  Host-only; bytes is written on success.
  */
 cru_status cru_usp_workspace_bytes(const cru_tensor* q, int ulysses_degree,
                                    int ring_degree, size_t* bytes);

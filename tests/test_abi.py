@@ -142,6 +142,42 @@ def test_valid_call_reaches_device_check_without_gpu():
     assert st == EDEVICE, last_error()
 
 
+def test_broadcast_and_overlapping_inputs_pass_host_checks():
+    # inputs may repeat elements: k and v broadcast along the sequence
+    # (stride 0, what torch's expand() gives) or rows that overlap (stride
+    # below D); such calls pass every host check and stop at the fake pointer
+    q = T()
+    kb = T(S=24, strides=(0, 0, 64))
+    assert fwd(q, kb, kb, T(), L()) == EDEVICE, last_error()
+    kover = T(S=24, strides=(24 * 8 + 64 * 2, 8, 64))
+    assert fwd(q, kover, kover, T(), L()) == EDEVICE, last_error()
+    qb = T(strides=(0, 0, 0))
+    assert fwd(qb, T(S=24), T(S=24), T(), L()) == EDEVICE, last_error()
+
+
+@pytest.mark.parametrize("strides", [(16 * 2 * 64, 0, 64), (16 * 2 * 64, 64, 64),
+                                     (16 * 2 * 64, 2 * 64, 32), (16 * 2 * 64, 2 * 64, 0)])
+def test_overlapping_outputs_are_refused(strides):
+    # an output whose elements share addresses would have threads race on
+    # them: refused with CRU_EINVAL before anything is enqueued
+    o = T(strides=strides)
+    assert fwd(T(), T(S=24), T(S=24), o) == EINVAL
+    assert "overlap" in last_error()
+    assert merge([T(dtype=cru.F32)], [L()], o) == EINVAL
+    assert h2s([T(S=16, H=2, strides=strides)], 2) == EINVAL
+
+
+def test_overlapping_lse_is_refused():
+    lse = cru.CruLse(FAKE, 1, 2, 16, 2 * 16, 8)       # heads 8 apart, rows of 16
+    assert fwd(T(), T(S=24), T(S=24), T(), lse) == EINVAL
+    assert "overlap" in last_error()
+    lse = cru.CruLse(FAKE, 2, 2, 16, 16, 16)          # batch 1 lands on head 1
+    assert fwd(T(B=2), T(B=2, S=24), T(B=2, S=24), T(B=2), lse) == EINVAL
+    # head-major or padded layouts are fine
+    lse = cru.CruLse(FAKE, 2, 2, 16, 16, 32)          # [H, B, S] storage
+    assert fwd(T(B=2), T(B=2, S=24), T(B=2, S=24), T(B=2), lse) == EDEVICE, last_error()
+
+
 def test_empty_query_is_a_no_op():
     st = fwd(T(S=0, data=0), T(S=24), T(S=24), T(S=0, data=0), L(S=0, data=0))
     assert st == OK, last_error()
@@ -212,6 +248,11 @@ def test_ring_validation():
     assert ring(q, k, v, 2, anything=1, sizes=[20, 17]) == EDEVICE
     assert ring(q, k, v, 2, anything=1, sizes=[20, 16]) == EINVAL   # sum != Skv
     assert ring(q, k, v, 2, anything=1, sizes=[38, -1]) == EINVAL
+    # sizes whose int64 sum wraps around to Skv are refused chunk by chunk
+    big = (1 << 63) - 1
+    assert ring(q, k, v, 3, anything=1, sizes=[big, big, 39]) == EINVAL
+    assert "pass the 37 K/V rows" in last_error()
+    assert ring(q, k, v, 3, anything=1, sizes=[10, 30, -3]) == EINVAL
     assert ring(q, k, v, 0) == EINVAL
     assert ring(q, k, v, 1, anything=2) == EINVAL
     assert ring(q, k, v, 1, fused=3) == EINVAL

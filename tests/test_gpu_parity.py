@@ -62,6 +62,22 @@ def inputs(idx):
     return (q, k, v), tuple(cuda(q, k, v))
 
 
+@functools.lru_cache(maxsize=4)
+def oracle_full(idx):
+    """The oracle's attention over every row of a workload (fp64)."""
+    (q, k, v), _ = inputs(idx)
+    return oracle.attention(to_f64(q), to_f64(k), to_f64(v))
+
+
+def check_all(o_gpu, l_gpu, o_ref, l_ref, tol_o, tol_l, what):
+    """Every element of O and LSE against the oracle."""
+    eo = err(to_f64(o_gpu), o_ref)
+    el = err(to_f64(l_gpu), l_ref)
+    say(f"  {what}: max|dO| = {eo:.3e}, max|dLSE| = {el:.3e} over all {o_ref.shape[1]} rows")
+    assert eo <= tol_o, f"{what}: O error {eo}"
+    assert el <= tol_l, f"{what}: LSE error {el}"
+
+
 def sample_rows(S, n=48, seed=0):
     rng = np.random.default_rng(seed)
     fixed = [0, 1, 31, 32, 63, 64, 127, 128, 129, 255, 256, 257, S // 2, S - 2, S - 1]
@@ -148,12 +164,8 @@ def test_bf16_workgroup_shapes(H, waves, D, out_dtype):
     say(f"bf16 H={H} (expect {waves}-wave workgroups) D={D} out={out_dtype}")
     o, l = cru.attn_fwd_lse(*cuda(q, k, v), out_dtype=out_dtype)
     torch.cuda.synchronize()
-    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
-    heads = sorted({0, 1, H // 2, H - 1})
-    rows = sample_rows(300)
-    for h in heads:
-        check_rows(o[:, :, h:h + 1], l[:, h:h + 1], q64[:, :, h:h + 1], k64[:, :, h:h + 1],
-                   v64[:, :, h:h + 1], rows, TOL_O, TOL_LSE, f"head {h}")
+    o_ref, l_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v))
+    check_all(o, l, o_ref, l_ref, TOL_O, TOL_LSE, f"H={H}, every head")
 
 
 @pytest.mark.parametrize("shape", [(1, 10, 10, 8, 64), (1, 1, 1, 1, 128), (3, 1, 700, 2, 64),
@@ -179,6 +191,56 @@ def test_strided_views_and_scale():
     o_ref, l_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), scale=0.05)
     assert err(to_f64(o), o_ref) <= TOL_O
     assert err(to_f64(l), l_ref) <= TOL_LSE
+
+
+def _views(base, shape, strides, dev):
+    """The same strided view of one buffer on the device and on the host."""
+    return (torch.as_strided(base.to(dev), shape, strides),
+            torch.as_strided(base, shape, strides))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_broadcast_and_overlapping_input_views(D, dtype):
+    # Inputs whose elements repeat: K and V expand()-ed along the sequence
+    # (stride 0: one key row seen Skv times), Q expanded likewise, and rows
+    # that overlap (sequence stride 8 elements < D).  Every element against
+    # the oracle on the same values made contiguous.
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tol_o, tol_l = (TOL_O, TOL_LSE) if dtype == "bf16" else (TOL_F32, TOL_F32)
+    g = torch.Generator().manual_seed(60 + D)
+    B, Sq, Skv, H = 2, 200, 300, 3
+    q, k, v = random_qkv(61 + D, B, Sq, Skv, H, D, gain=math.sqrt(3.0), dtype=dtype)
+    cases = {}
+    # k, v: one row per (b, h), broadcast over all 300 keys.  Every key then
+    # gets the same weight and O = v exactly; in fp32 the kernel sums 300
+    # equal terms for the numerator and for the denominator, each within
+    # (Skv - 1) * 2^-24 relative, so O is within twice that of v (the bound
+    # the constant-V test derives), above 1e-5 once |v| passes about 0.6
+    k1 = k[:, :1].expand(B, Skv, H, D)
+    v1 = v[:, :1].expand(B, Skv, H, D)
+    assert k1.stride(1) == 0
+    tol_rep = max(tol_o, 2 * (Skv - 1) * 2.0 ** -24 * float(v1.float().abs().max()))
+    cases["k, v expand()-ed along S"] = (q.cuda(), k1.cuda(), v1.cuda(), q, k1, v1, tol_rep)
+    # q broadcast as well (all query rows equal)
+    q1 = q[:, :1].expand(B, Sq, H, D)
+    cases["q, k, v expand()-ed along S"] = (q1.cuda(), k1.cuda(), v1.cuda(), q1, k1, v1,
+                                            tol_rep)
+    # overlapping rows: row s starts 8 elements after row s-1
+    n = (Skv - 1) * 8 + D
+    shape, strides = (B, Skv, H, D), (H * n, 8, n, 1)
+    kb = torch.randn(B * H * n, generator=g).to(tdt)
+    vb = torch.randn(B * H * n, generator=g).to(tdt)
+    kd, kh = _views(kb, shape, strides, "cuda")
+    vd, vh = _views(vb, shape, strides, "cuda")
+    cases["k, v rows overlapping (stride 8)"] = (q.cuda(), kd, vd, q, kh, vh, tol_o)
+    for what, (qd, kd, vd, qh, kh, vh, tol) in cases.items():
+        say(f"{what}: D={D} {dtype}")
+        o, l = cru.attn_fwd_lse(qd, kd, vd, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.attention(to_f64(qh.contiguous()), to_f64(kh.contiguous()),
+                                        to_f64(vh.contiguous()))
+        check_all(o, l, o_ref, l_ref, tol, tol_l, what)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -526,8 +588,9 @@ def test_ulysses_anything_share_bitwise(P):
     assert torch.equal(back, o_full)
     q2, k2, v2 = (oracle.head_groups(to_f64(t), P)[1] for t in (q, k, v))
     h0, h1 = cru.ulysses_head_bounds(H, P, anything=True)[1]
-    check_rows(o_full[:, :, h0:h1], l_full[:, h0:h1], q2, k2, v2, sample_rows(S, 16, seed=P),
-               TOL_O, TOL_LSE, f"{w.name} anything group 1")
+    o_ref, l_ref = oracle.attention(q2, k2, v2)
+    check_all(o_full[:, :, h0:h1], l_full[:, h0:h1], o_ref, l_ref, TOL_O, TOL_LSE,
+              f"{w.name} anything group 1")
 
 
 # ------------------------------------------------ Unified (USP) attention
@@ -557,8 +620,8 @@ def test_usp_bf16_workloads(idx, Pu, Pr):
     # against the unchunked GPU forward: same result up to the fold's rounding
     assert err(to_f64(o_s), to_f64(o_full)) <= TOL_PAIR_O
     assert err(to_f64(l_s), to_f64(l_full)) <= TOL_PAIR_LSE
-    check_rows(o_s, l_s, to_f64(q), to_f64(k), to_f64(v), sample_rows(w.S, 24, seed=Pu * Pr),
-               TOL_O, TOL_LSE, f"usp {w.name}")
+    o_ref, l_ref = oracle_full(idx)
+    check_all(o_s, l_s, o_ref, l_ref, TOL_O, TOL_LSE, f"usp {w.name}")
 
 
 # --------------------------------- partials in the model dtype (bf16)
@@ -584,13 +647,9 @@ def test_ring_bf16_partials(fused):
     # the LSE does not depend on the partials' dtype
     assert torch.equal(l16, l32)
     assert err(to_f64(o16), to_f64(o32)) <= tol + TOL_O
-    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
-    rows = sample_rows(b - a, 32, seed=3)
-    o_ref, l_ref = oracle.attention(q64[:, a:b][:, rows], k64, v64)
-    eo = err(to_f64(o16)[:, rows], o_ref)
-    say(f"  bf16 partials: max|dO| = {eo:.3e} (bound {tol:.3e})")
-    assert eo <= tol
-    assert err(to_f64(l16)[:, :, rows], l_ref) <= TOL_LSE
+    o_ref, l_ref = oracle_full(3)
+    check_all(o16, l16, o_ref[:, a:b], l_ref[:, :, a:b], tol, TOL_LSE,
+              f"bf16 partials (O bound {tol:.3e})")
 
 
 def test_ring_bf16_partials_fused_equals_stepwise_and_anything():
@@ -601,8 +660,9 @@ def test_ring_bf16_partials_fused_equals_stepwise_and_anything():
                                 convert_to_fp32=False)
     torch.cuda.synchronize()
     assert torch.equal(o_s, o_f) and torch.equal(l_s, l_f)
-    check_rows(o_s, l_s, to_f64(q), to_f64(k), to_f64(v), sample_rows(w.S, 24, seed=41),
-               tol_bf16_partials(vd), TOL_LSE, "ring anything, bf16 partials")
+    o_ref, l_ref = oracle_full(4)
+    check_all(o_s, l_s, o_ref, l_ref, tol_bf16_partials(vd), TOL_LSE,
+              "ring anything, bf16 partials")
 
 
 def test_usp_bf16_partials():
@@ -610,8 +670,8 @@ def test_usp_bf16_partials():
     (q, k, v), (qd, kd, vd) = inputs(2)
     o, l = cru.usp_emulate(qd, kd, vd, 2, 3, fused=True, convert_to_fp32=False)
     torch.cuda.synchronize()
-    check_rows(o, l, to_f64(q), to_f64(k), to_f64(v), sample_rows(w.S, 24, seed=42),
-               tol_bf16_partials(vd), TOL_LSE, "usp 2 x 3, bf16 partials")
+    o_ref, l_ref = oracle_full(2)
+    check_all(o, l, o_ref, l_ref, tol_bf16_partials(vd), TOL_LSE, "usp 2 x 3, bf16 partials")
 
 
 # ------------------------------------------------- the five workloads, full size
@@ -624,8 +684,8 @@ def test_workload_full_forward(idx):
     o, l = cru.attn_fwd_lse(qd, kd, vd)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all().item() and torch.isfinite(l).all().item()
-    check_rows(o, l, to_f64(q), to_f64(k), to_f64(v), sample_rows(w.S, seed=idx),
-               TOL_O, TOL_LSE, w.name)
+    o_ref, l_ref = oracle_full(idx)
+    check_all(o, l, o_ref, l_ref, TOL_O, TOL_LSE, w.name)
 
 
 def test_degree_sweep_same_seed():
@@ -633,14 +693,13 @@ def test_degree_sweep_same_seed():
     # every degree.  Ulysses: the regrouped shares, put back together, are
     # bit-identical to the full forward at every degree.  Ring: every rank's
     # share assembled agrees with degree 1 within twice the bar (both are
-    # within it of the exact result) and with the oracle on sampled rows.
+    # within it of the exact result) and with the oracle on every row.
     w = workload(2)
     (q, k, v), (qd, kd, vd) = inputs(2)
     S, H = w.S, w.H
     o1, l1 = cru.attn_fwd_lse(qd, kd, vd)
     torch.cuda.synchronize()
-    rows = sample_rows(S, 16, seed=3)
-    o_ref, l_ref = oracle.attention(to_f64(q)[:, rows], to_f64(k), to_f64(v))
+    o_ref, l_ref = oracle_full(2)
     for P in (1, 2, 4, 8):
         say(f"degree sweep: Ulysses P={P}")
         ys = cru.ulysses_seq2head([qd, kd, vd], P)
@@ -661,8 +720,7 @@ def test_degree_sweep_same_seed():
         torch.cuda.synchronize()
         assert err(to_f64(o_n), to_f64(o1)) <= TOL_PAIR_O, N
         assert err(to_f64(l_n), to_f64(l1)) <= TOL_PAIR_LSE, N
-        assert err(to_f64(o_n)[:, rows], o_ref) <= TOL_O, N
-        assert err(to_f64(l_n)[:, :, rows], l_ref) <= TOL_LSE, N
+        check_all(o_n, l_n, o_ref, l_ref, TOL_O, TOL_LSE, f"ring degree {N}, all ranks")
 
 
 @pytest.mark.parametrize("idx", [2, 5])
@@ -685,10 +743,12 @@ def test_ulysses_share_matches_full_forward_bitwise(idx):
     o_back = cru.ulysses_head2seq(torch.stack(o_groups), P)
     torch.cuda.synchronize()
     assert torch.equal(o_back, o_full)
-    # and the share itself against the oracle (group 0, sampled rows)
+    # and the share itself against the oracle's attention on the regrouped
+    # heads (group 0, every row)
     q0, k0, v0 = (oracle.seq2head(to_f64(t), P)[0] for t in (q, k, v))
-    check_rows(o_groups[0], l_full[:, :Hp], q0, k0, v0, sample_rows(w.S, 24, seed=idx),
-               TOL_O, TOL_LSE, f"{w.name} ulysses group 0")
+    o_ref, l_ref = oracle.attention(q0, k0, v0)
+    check_all(o_groups[0], l_full[:, :Hp], o_ref, l_ref, TOL_O, TOL_LSE,
+              f"{w.name} ulysses group 0")
 
 
 @pytest.mark.parametrize("rank", [0, 5, 7])
@@ -703,15 +763,12 @@ def test_flux1024_ring_share(rank):
     torch.cuda.synchronize()
     assert torch.equal(o_s, o_f) and torch.equal(l_s, l_f)   # same per-chunk code
     q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
-    rows = sample_rows(b - a, 32, seed=rank)
-    # the unchunked definition for the sampled rows of the share
-    o_ref, l_ref = oracle.attention(q64[:, a:b][:, rows], k64, v64)
-    assert err(to_f64(o_s)[:, rows], o_ref) <= TOL_O
-    assert err(to_f64(l_s)[:, :, rows], l_ref) <= TOL_LSE
-    # the oracle's own ring share for the sampled rows, folded chunk by chunk
-    o_ring, l_ring = oracle.chunked_attention(q64[:, a:b][:, rows], k64, v64, N)
-    assert err(to_f64(o_s)[:, rows], o_ring) <= TOL_O
-    assert err(to_f64(l_s)[:, :, rows], l_ring) <= TOL_LSE
+    # every row of the share: the unchunked definition ...
+    o_ref, l_ref = oracle_full(3)
+    check_all(o_s, l_s, o_ref[:, a:b], l_ref[:, :, a:b], TOL_O, TOL_LSE, f"rank {rank} share")
+    # ... and the oracle's own ring share, folded chunk by chunk
+    o_ring, l_ring = oracle.ring_share(q64, k64, v64, N, rank)
+    check_all(o_s, l_s, o_ring, l_ring, TOL_O, TOL_LSE, f"rank {rank} share (oracle ring fold)")
 
 
 def test_flux1024_all_rows_chunked_merge():
@@ -725,8 +782,8 @@ def test_flux1024_all_rows_chunked_merge():
     el = err(to_f64(l_c), to_f64(l_full))
     say(f"  chunked+merged vs unchunked (GPU): max|dO| = {eo:.3e}, max|dLSE| = {el:.3e}")
     assert eo <= TOL_PAIR_O and el <= TOL_PAIR_LSE
-    check_rows(o_c, l_c, to_f64(q), to_f64(k), to_f64(v), sample_rows(w.S, 24, seed=30),
-               TOL_O, TOL_LSE, "flux-1024 chunked+merged")
+    o_ref, l_ref = oracle_full(3)
+    check_all(o_c, l_c, o_ref, l_ref, TOL_O, TOL_LSE, "flux-1024 chunked+merged")
 
 
 @pytest.mark.parametrize("fused", [False, True])
@@ -742,14 +799,15 @@ def test_ring_anything_uneven_chunks(fused):
     torch.cuda.synchronize()
     assert err(to_f64(o_c), to_f64(o_full)) <= TOL_PAIR_O
     assert err(to_f64(l_c), to_f64(l_full)) <= TOL_PAIR_LSE
-    check_rows(o_c, l_c, to_f64(q), to_f64(k), to_f64(v), sample_rows(w.S, 24, seed=40),
-               TOL_O, TOL_LSE, "ring anything chunked+merged")
+    o_ref, l_ref = oracle_full(4)
+    check_all(o_c, l_c, o_ref, l_ref, TOL_O, TOL_LSE, "ring anything chunked+merged")
     # rank 0's share: its 581 rows
     a, b = cru.ring_chunk_bounds(w.S, N, anything=True)[0]
     assert (a, b) == (0, 581)
     o_r, l_r = cru.ring_emulate(qd[:, a:b], kd, vd, N, anything=True, fused=fused)
     torch.cuda.synchronize()
     assert err(to_f64(o_r), to_f64(o_c)[:, a:b]) <= TOL_PAIR_O
+    check_all(o_r, l_r, o_ref[:, a:b], l_ref[:, :, a:b], TOL_O, TOL_LSE, "ring anything rank 0")
 
 
 @pytest.mark.parametrize("fused", [False, True])
