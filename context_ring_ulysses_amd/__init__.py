@@ -10,7 +10,7 @@ built.
 
 Entry points (same names as the C ABI without the ``cru_`` prefix):
     attn_fwd_lse, attn_merge_lse, ring_chunk_bounds, ring_workspace_bytes,
-    ring_emulate, ulysses_head_bounds, ulysses_seq2head, ulysses_head2seq,
+    ring_emulate, ring_emulate_noalloc, ulysses_head_bounds, ulysses_seq2head, ulysses_head2seq,
     usp_workspace_bytes, usp_emulate
 plus ulysses_groups (views of the head groups of a packed buffer).
 """
@@ -25,7 +25,7 @@ import torch
 
 __all__ = [
     "attn_fwd_lse", "attn_merge_lse", "ring_chunk_bounds", "ring_workspace_bytes",
-    "ring_emulate", "ulysses_head_bounds", "ulysses_seq2head", "ulysses_head2seq",
+    "ring_emulate", "ring_emulate_noalloc", "ulysses_head_bounds", "ulysses_seq2head", "ulysses_head2seq",
     "ulysses_groups", "usp_workspace_bytes", "usp_emulate", "ContextParallelConfig",
     "lib", "LIB_PATH", "CruError", "CruInvalid", "CruNotDivisible", "CruUnsupported",
     "CruDeviceError", "CruWorkspaceError", "CruHipError", "MAX_PARTS",
@@ -115,6 +115,10 @@ def lib() -> ctypes.CDLL:
                                    ctypes.c_int, ctypes.c_int, T, Lse, ctypes.c_float, vp,
                                    ctypes.c_size_t, vp]
     L.cru_ring_emulate.restype = st
+    L.cru_ring_emulate_noalloc.argtypes = [T, T, T, ctypes.c_int, ctypes.c_int,
+                                           _P(ctypes.c_int64), ctypes.c_int, ctypes.c_int, T, Lse,
+                                           ctypes.c_float, vp]
+    L.cru_ring_emulate_noalloc.restype = st
     L.cru_ulysses_head_bounds.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                           _P(ctypes.c_int64)]
     L.cru_ulysses_head_bounds.restype = st
@@ -275,6 +279,35 @@ def ring_emulate(q_share: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_chun
                                   ctypes.c_float(0.0 if scale is None else scale),
                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                   _stream(q_share)))
+    return out, lse
+
+
+def ring_emulate_noalloc(q_share: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         n_chunks: int, *, anything: bool = False,
+                         chunk_sizes: Optional[Sequence[int]] = None, fused: bool = False,
+                         convert_to_fp32: bool = True, out: Optional[torch.Tensor] = None,
+                         lse: Optional[torch.Tensor] = None,
+                         out_dtype: Optional[torch.dtype] = None, scale: Optional[float] = None,
+                         return_lse: bool = True
+                         ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """ring_emulate with the partials in the library's static scratch array
+    (no workspace; the C call allocates nothing).  Pass ``out`` (and ``lse``)
+    to keep this wrapper from allocating them as well."""
+    if out is None:
+        out = torch.empty(q_share.shape, dtype=out_dtype or q_share.dtype, device=q_share.device)
+    if lse is None and return_lse:
+        lse = _empty_lse(q_share.shape[0], q_share.shape[2], q_share.shape[1], q_share.device)
+    sizes = None
+    if chunk_sizes is not None:
+        if len(chunk_sizes) != n_chunks:
+            raise CruInvalid(1, f"{len(chunk_sizes)} chunk sizes for {n_chunks} chunks")
+        sizes = (ctypes.c_int64 * len(chunk_sizes))(*[int(x) for x in chunk_sizes])
+    qd, kd, vd = _desc(q_share, "q_share"), _desc(k, "k"), _desc(v, "v")
+    od, ld = _desc(out, "out"), _lse_desc(lse, "lse")
+    _check(lib().cru_ring_emulate_noalloc(qd, kd, vd, n_chunks, int(bool(anything)), sizes,
+                                          int(bool(fused)), int(bool(convert_to_fp32)), od,
+                                          _ref(ld), ctypes.c_float(0.0 if scale is None else scale),
+                                          _stream(q_share)))
     return out, lse
 
 

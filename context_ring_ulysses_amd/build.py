@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libcru.so")
 ARCH = "gfx950"
 
 SOURCES = ["attn_fwd_bf16.hip", "attn_fwd_f32.hip", "merge_lse.hip",
-           "ulysses_layout.hip", "cru_api.cpp"]
+           "ulysses_layout.hip", "ring_noalloc.hip", "cru_api.cpp"]
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

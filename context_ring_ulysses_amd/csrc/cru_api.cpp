@@ -396,6 +396,30 @@ cru_status cru_ring_emulate(const cru_tensor* q_share, const cru_tensor* k, cons
                             float scale, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
   g_err[0] = '\0';
+  return cru::ring_emulate_ws(q_share, k, v, n_chunks, anything, chunk_sizes, fused,
+                              convert_to_fp32, o, lse, scale, workspace, workspace_bytes, nullptr,
+                              stream);
+}
+
+}  // extern "C"
+
+namespace cru {
+
+cru_status report(cru_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+cru_status ring_emulate_ws(const cru_tensor* q_share, const cru_tensor* k, const cru_tensor* v,
+                           int n_chunks, int anything, const int64_t* chunk_sizes, int fused,
+                           int convert_to_fp32, const cru_tensor* o, const cru_lse* lse,
+                           float scale, void* workspace, size_t workspace_bytes,
+                           ScratchFn scratch, hipStream_t stream) {
   CRU_TRY(check_qkvo(q_share, k, v, o));
   if (lse != nullptr) CRU_TRY(check_lse(lse, "lse", q_share->B, q_share->H, q_share->S));
   if (n_chunks < 1 || n_chunks > CRU_MAX_PARTS)
@@ -436,11 +460,18 @@ cru_status cru_ring_emulate(const cru_tensor* q_share, const cru_tensor* k, cons
 
   size_t need = 0;
   CRU_TRY(cru_ring_workspace_bytes(q_share, n_chunks, &need));
-  if (need > 0 && workspace == nullptr) return fail(CRU_EWORKSPACE, "workspace is NULL");
-  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-    return fail(CRU_EWORKSPACE, "workspace is not 256-byte aligned");
-  if (workspace_bytes < need)
-    return fail(CRU_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  if (scratch != nullptr) {
+    if (need > workspace_bytes)
+      return fail(CRU_EWORKSPACE,
+                  "the share needs %zu bytes of partials; the library's static scratch holds %zu",
+                  need, workspace_bytes);
+  } else {
+    if (need > 0 && workspace == nullptr) return fail(CRU_EWORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+      return fail(CRU_EWORKSPACE, "workspace is not 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(CRU_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  }
 
   const int64_t rows = q_share->B * q_share->H * q_share->S;
   if (rows == 0) return CRU_OK;
@@ -449,7 +480,10 @@ cru_status cru_ring_emulate(const cru_tensor* q_share, const cru_tensor* k, cons
   CRU_TRY(check_device(v->data, "v"));
   CRU_TRY(check_device(o->data, "o"));
   if (lse != nullptr) CRU_TRY(check_device(lse->data, "lse"));
-  CRU_TRY(check_device(workspace, "workspace"));
+  if (scratch != nullptr)
+    CRU_TRY(scratch(&workspace));   // the current device's static array
+  else
+    CRU_TRY(check_device(workspace, "workspace"));
 
   // Partials in the workspace: n [B, Sq, H, D] outputs (fp32, or bf16 without
   // convert_to_fp32), then n fp32 [B, H, Sq] LSEs.
@@ -505,6 +539,10 @@ cru_status cru_ring_emulate(const cru_tensor* q_share, const cru_tensor* k, cons
   m.o_f32 = o->dtype == CRU_F32;
   return hip_status(cru::launch_merge(m, stream), "ring merge launch");
 }
+
+}  // namespace cru
+
+extern "C" {
 
 static cru_status layout_common(int n, const cru_tensor* x, int P, int anything,
                                 const char* what, cru::LayoutArgs* a) {

@@ -68,6 +68,19 @@ struct LayoutArgs {
   FastDiv div_h, div_s, div_hp, div_b, div_q, div_q1;
 };
 
+// Host side shared by the C entry points.  ScratchFn hands back the current
+// device's static scratch array (ring_noalloc.hip); with it,
+// ring_emulate_ws takes workspace_bytes as that array's size and skips the
+// workspace pointer checks.  report() sets the thread's error message.
+typedef cru_status (*ScratchFn)(void** ptr);
+cru_status ring_emulate_ws(const cru_tensor* q_share, const cru_tensor* k, const cru_tensor* v,
+                           int n_chunks, int anything, const int64_t* chunk_sizes, int fused,
+                           int convert_to_fp32, const cru_tensor* o, const cru_lse* lse,
+                           float scale, void* workspace, size_t workspace_bytes,
+                           ScratchFn scratch, hipStream_t stream);
+cru_status report(cru_status st, const char* fmt, ...);
+void clear_error();
+
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);

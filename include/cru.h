@@ -224,6 +224,34 @@ cru_status cru_ring_emulate(const cru_tensor* q_share, const cru_tensor* k,
                             size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * cru_ring_emulate_noalloc -- cru_ring_emulate without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The
+ * partials go to a static device array of CRU_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends; nothing is
+ * allocated or freed by the call.
+ *
+ *   arguments    as for cru_ring_emulate, without workspace/workspace_bytes
+ *   limit        cru_ring_workspace_bytes(q_share, n_chunks) must not exceed
+ *                CRU_NOALLOC_SCRATCH_BYTES (CRU_EWORKSPACE otherwise, before
+ *                anything is enqueued): 64 MiB holds, for example, an 8-chunk
+ *                share of 576 rows x 24 heads x 128 dims
+ *   results      identical to cru_ring_emulate's with the same arguments
+ * Every call on one GPU shares that GPU's array, and the array keeps the
+ * last call's partials (the call writes every partial it reads, so nothing
+ * needs clearing).  Calls that overlap in time on one GPU (different
+ * streams, or threads without ordering) race on the array: order them on
+ * one stream.
+ */
+#define CRU_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+cru_status cru_ring_emulate_noalloc(const cru_tensor* q_share, const cru_tensor* k,
+                                    const cru_tensor* v, int n_chunks, int anything,
+                                    const int64_t* chunk_sizes, int fused,
+                                    int convert_to_fp32, const cru_tensor* o,
+                                    const cru_lse* lse, float scale,
+                                    hipStream_t stream);
+
+/*
  * cru_ulysses_head_bounds -- the heads of each Ulysses group: group p holds
  * heads [starts[p], starts[p+1]).  The first H mod P groups get one head
  * more (sizes differ by at most one).  With anything = 0, H must be

@@ -274,6 +274,30 @@ def test_ring_validation():
     assert ring(q, k, v, 4, anything=1, fp32=2) == EINVAL
 
 
+def ring_na(q, k, v, n, anything=0, fused=0, fp32=1):
+    o = T(S=q.S, H=q.H, D=q.D, dtype=q.dtype)
+    return cru.lib().cru_ring_emulate_noalloc(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                                              n, anything, None, fused, fp32, ctypes.byref(o),
+                                              None, ctypes.c_float(0.0), None)
+
+
+def test_ring_noalloc_validation():
+    # the same host checks as cru_ring_emulate, then the scratch size limit,
+    # all before any device call (the fake pointers stop it at the device check)
+    q, k, v = T(S=10), T(S=37), T(S=37)
+    assert ring_na(q, k, v, 8) == ENOTDIV
+    assert ring_na(q, k, v, 8, anything=1) == EDEVICE, last_error()
+    # 8 fp32 partials of 1024 x 24 x 128 need 8 * 12.6 MB > 64 MiB
+    big_q = T(S=1024, H=24, D=128)
+    big_kv = T(S=8192, H=24, D=128)
+    assert ring_na(big_q, big_kv, big_kv, 8) == EWORKSPACE
+    assert "static scratch" in last_error()
+    # FLUX-1024's ring share (576 rows x 24 heads, 8 chunks) fits
+    share = T(S=576, H=24, D=128)
+    kv = T(S=4608, H=24, D=128)
+    assert ring_na(share, kv, kv, 8) == EDEVICE, last_error()
+
+
 def s2h(xs, P, ys=None, anything=0):
     n = len(xs)
     X = (cru.CruTensor * n)(*xs)
