@@ -9,19 +9,23 @@ attention shape (B=1, H=24, S=4096+512=4608, D=128, bf16, synthetic inputs):
      per-chunk partials from one split-KV launch, then the in-order fold
      (bitwise the same result as one launch per chunk);
   3. the 8-way LSE merge over all 4608 rows (8 fp32 partials -> bf16 O);
-  4. Ulysses rank 0's share at degree 2: seq2head of Q, K, V, attention over
-     its 12 heads at full length, head2seq of the output.
+  4. Ulysses rank 0's share at degree 2: seq2head of Q, K, V, then attention
+     over its 12 heads at full length whose epilogue stores straight into
+     those heads of the [B, S, H, D] output (the regrouping by token fused
+     into the store; the standalone head2seq kernel is timed cold below).
 
 Inputs (and the merge's partials) are resident in HBM before timing starts.
 ``value`` is the attention work of a step (4*B*H*Sq*Skv*D summed over parts
 1, 2 and 4) divided by the step time.  The JSON line also carries each
 part's own time, the attention kernel's roofline (achieved TFLOP/s from HIP
-events on its stream vs the bf16 dense peak), cold-cache bandwidth of the
-merge and layout kernels, and the fp64 oracle timed on the host cores.
+events on its stream, 100 timed launches of the full forward on their own,
+vs the bf16 dense peak), cold-cache bandwidth of the merge and layout
+kernels, and the fp64 oracle timed on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
     python bench.py --copy-calibration   # plain copy of known size, for counters
     python bench.py --attn-only N        # N FLUX-1024 forwards only, for counters
+    python bench.py --load-sweep         # FLUX-1024-shaped forward at 1..48 heads
 """
 from __future__ import annotations
 
@@ -151,12 +155,51 @@ def attn_only(n):
     log(f"[bench] {n} FLUX-1024 forwards done")
 
 
+def load_sweep():
+    """The S=4608, D=128 forward at several head counts: time per workgroup
+    key tile as the number of busy CUs grows (18 workgroups of 256 query
+    rows per head; 256 CUs)."""
+    import torch
+    import context_ring_ulysses_amd as cru
+    S, D = 4608, 128
+    g = torch.Generator(device="cuda").manual_seed(0)
+    rows = []
+    for H in (1, 2, 4, 7, 10, 14, 24, 48):
+        q = (torch.randn(1, S, H, D, device="cuda", generator=g) * 3 ** 0.5).to(torch.bfloat16)
+        k = (torch.randn(1, S, H, D, device="cuda", generator=g) * 3 ** 0.5).to(torch.bfloat16)
+        v = torch.randn(1, S, H, D, device="cuda", generator=g).to(torch.bfloat16)
+        o = torch.empty_like(q)
+        l = torch.empty(1, H, S, device="cuda")
+        for _ in range(5):
+            cru.attn_fwd_lse(q, k, v, out=o, lse=l)
+        ts = []
+        for _ in range(50):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            cru.attn_fwd_lse(q, k, v, out=o, lse=l)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        t = statistics.median(ts)
+        wgs = 18 * H
+        rounds = -(-wgs // 256)
+        rows.append({"heads": H, "workgroups": wgs, "ms_median": t,
+                     "TFLOP/s": attn_flops(1, H, S, S, D) / (t * 1e-3) / 1e12,
+                     "us_per_workgroup_tile": t * 1e3 / rounds / (S // 64)})
+        log(f"[bench] load sweep H={H}: {rows[-1]}")
+    print(json.dumps({"load_sweep": rows}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cold-reps", type=int, default=20)
+    ap.add_argument("--cold-reps", type=int, default=50)
+    ap.add_argument("--attn-reps", type=int, default=100,
+                    help="timed launches of the full forward for the roofline leg")
+    ap.add_argument("--load-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--attn-only", type=int, default=0, metavar="N",
@@ -177,6 +220,9 @@ def main():
         return
     if args.attn_only:
         attn_only(args.attn_only)
+        return
+    if args.load_sweep:
+        load_sweep()
         return
 
     dev = torch.device("cuda:0")
@@ -205,7 +251,6 @@ def main():
     o_merge = torch.empty_like(q)
     l_merge = torch.empty(B, H, S, dtype=torch.float32, device=dev)
     ys = [torch.empty(P, B, S, Hp, D, dtype=q.dtype, device=dev) for _ in range(3)]
-    o_groups = torch.zeros(P, B, S, Hp, D, dtype=q.dtype, device=dev)
     l_u = torch.empty(B, Hp, S, dtype=torch.float32, device=dev)
     o_u = torch.empty_like(q)
     torch.cuda.synchronize()
@@ -223,8 +268,9 @@ def main():
         cru.attn_merge_lse(parts_o, parts_l, out=o_merge, lse=l_merge)
         if m: m[3].record(stream)
         cru.ulysses_seq2head([q, k, v], P, out=ys)
-        cru.attn_fwd_lse(ys[0][0], ys[1][0], ys[2][0], out=o_groups[0], lse=l_u)
-        cru.ulysses_head2seq(o_groups, P, out=o_u)
+        # group 0's heads of the [B, S, H, D] output: a strided view the
+        # epilogue stores into directly (head2seq of this group, fused)
+        cru.attn_fwd_lse(ys[0][0], ys[1][0], ys[2][0], out=o_u[:, :, :Hp], lse=l_u)
         if m: m[4].record(stream)
 
     for _ in range(args.warmup):
@@ -274,6 +320,27 @@ def main():
 
     med, mn = cold(lambda: cru.attn_merge_lse(parts_o, parts_l, out=o_merge, lse=l_merge),
                    args.cold_reps)
+    # the roofline leg: the full forward on its own, timed launch by launch
+    # on the library's stream (torch's current stream) after about a second
+    # of back-to-back forwards, so the clocks have settled where a running
+    # job holds them
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < 1.0:
+        for _ in range(20):
+            cru.attn_fwd_lse(q, k, v, out=o_full, lse=l_full)
+        torch.cuda.synchronize()
+    attn_ts = []
+    for _ in range(args.attn_reps):
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        cru.attn_fwd_lse(q, k, v, out=o_full, lse=l_full)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        attn_ts.append(e0.elapsed_time(e1))
+    attn_mean = statistics.mean(attn_ts)
+    log(f"[bench] full forward alone: {args.attn_reps} launches, mean {attn_mean * 1e3:.1f} us, "
+        f"median {statistics.median(attn_ts) * 1e3:.1f} us, min {min(attn_ts) * 1e3:.1f} us")
+
     cold_merge = {"workload": "flux-1024, 8 fp32 partials over all 4608 rows -> bf16 O + LSE",
                   "bytes": mbytes, "ms_median": med, "ms_min": mn,
                   "GB/s": mbytes / (med * 1e-3) / 1e9,
@@ -439,11 +506,17 @@ def main():
     torch.cuda.synchronize()
 
     traffic = counters_traffic()
+    achieved = f_full / (attn_mean * 1e-3) / 1e12
     roofline = {"kernel": "attn_fwd_bf16 (full forward, FLUX-1024)", "bound": "mfma",
-                "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "algorithmic_flops_per_launch": f_full,
-                "avg_launch_ms": part_ms["attn_full"]}
+                "avg_launch_ms": attn_mean,
+                "launches_timed": args.attn_reps,
+                "median_launch_ms": statistics.median(attn_ts),
+                "min_launch_ms": min(attn_ts),
+                "frac_at_min": f_full / (min(attn_ts) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                "in_step_avg_launch_ms": part_ms["attn_full"]}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -459,7 +532,8 @@ def main():
         "config": {"workload": "flux-1024", "B": B, "H": H, "S": S, "D": D,
                    "ring_degree": N, "ulysses_degree": P,
                    "step": "full forward + ring rank-0 share (8 chunks, one split-KV launch) + "
-                           "8-way merge over all rows + Ulysses rank-0 share (P=2)",
+                           "8-way merge over all rows + Ulysses rank-0 share (P=2, output "
+                           "stored straight into its heads of [B, S, H, D])",
                    "step_attention_flops": step_flops},
         "roofline": roofline,
         "cpu_baseline": cpu,
