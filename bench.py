@@ -25,6 +25,7 @@ kernels, and the fp64 oracle timed on the host cores.
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
     python bench.py --copy-calibration   # plain copy of known size, for counters
     python bench.py --attn-only N        # N FLUX-1024 forwards only, for counters
+    python bench.py --attn-only N --heads H   # the same shape with H heads
     python bench.py --load-sweep         # FLUX-1024-shaped forward at 1..48 heads
 """
 from __future__ import annotations
@@ -140,19 +141,25 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}))
 
 
-def attn_only(n):
-    """n full forwards at FLUX-1024 and nothing else, for counter collection."""
+def attn_only(n, heads=0):
+    """n full forwards at FLUX-1024 and nothing else, for counter collection.
+    heads > 0: the same shape (S=4608, D=128) with that many heads instead,
+    to see how the counters change with the number of busy CUs (18
+    workgroups of 256 query rows per head)."""
     import torch
     import context_ring_ulysses_amd as cru
-    from workloads import make_inputs, workload
+    from workloads import make_inputs, random_qkv, workload
     w = workload(3)
-    q, k, v = (t.cuda() for t in make_inputs(3))
+    if heads > 0:
+        q, k, v = (t.cuda() for t in random_qkv(11, 1, w.S, w.S, heads, w.D, gain=3 ** 0.5))
+    else:
+        q, k, v = (t.cuda() for t in make_inputs(3))
     o = torch.empty_like(q)
-    l = torch.empty(w.B, w.H, w.S, dtype=torch.float32, device=q.device)
+    l = torch.empty(q.shape[0], q.shape[2], q.shape[1], dtype=torch.float32, device=q.device)
     for _ in range(n):
         cru.attn_fwd_lse(q, k, v, out=o, lse=l)
     torch.cuda.synchronize()
-    log(f"[bench] {n} FLUX-1024 forwards done")
+    log(f"[bench] {n} forwards done, {q.shape[2]} heads")
 
 
 def load_sweep():
@@ -204,6 +211,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--attn-only", type=int, default=0, metavar="N",
                     help="run N FLUX-1024 full forwards and exit (for counter passes)")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="with --attn-only: this many heads instead of 24")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -219,7 +228,7 @@ def main():
         copy_calibration()
         return
     if args.attn_only:
-        attn_only(args.attn_only)
+        attn_only(args.attn_only, args.heads)
         return
     if args.load_sweep:
         load_sweep()
