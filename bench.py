@@ -329,23 +329,24 @@ def main():
 
     med, mn = cold(lambda: cru.attn_merge_lse(parts_o, parts_l, out=o_merge, lse=l_merge),
                    args.cold_reps)
-    # the roofline leg: the full forward on its own, timed launch by launch
-    # on the library's stream (torch's current stream) after about a second
-    # of back-to-back forwards, so the clocks have settled where a running
-    # job holds them
+    # the roofline leg: the full forward on its own, each launch timed by the
+    # events around it on the library's stream (torch's current stream),
+    # after about a second of back-to-back forwards, so the clocks have
+    # settled where a running job holds them
     t_warm = time.perf_counter()
     while time.perf_counter() - t_warm < 1.0:
         for _ in range(20):
             cru.attn_fwd_lse(q, k, v, out=o_full, lse=l_full)
         torch.cuda.synchronize()
-    attn_ts = []
-    for _ in range(args.attn_reps):
-        e0, e1 = ev(), ev()
-        e0.record(stream)
+    # back to back: an event after every launch, so consecutive events
+    # bracket exactly one forward and no host sync sits between launches
+    evs = [ev() for _ in range(args.attn_reps + 1)]
+    evs[0].record(stream)
+    for i in range(args.attn_reps):
         cru.attn_fwd_lse(q, k, v, out=o_full, lse=l_full)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        attn_ts.append(e0.elapsed_time(e1))
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    attn_ts = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.attn_reps)]
     attn_mean = statistics.mean(attn_ts)
     log(f"[bench] full forward alone: {args.attn_reps} launches, mean {attn_mean * 1e3:.1f} us, "
         f"median {statistics.median(attn_ts) * 1e3:.1f} us, min {min(attn_ts) * 1e3:.1f} us")
@@ -408,17 +409,27 @@ def main():
                        "GB/s": 2 * tbytes / (meda2 * 1e-3) / 1e9,
                        "frac_hbm_peak": 2 * tbytes / (meda2 * 1e-3) / 1e9 / PEAK_HBM_GBS}}
 
-    def warm(fn, reps=20):
-        for _ in range(3):
-            fn()
+    def warm(fn, reps=10, batch=10):
+        # back to back, as a running job issues them: after a settling
+        # quarter second, `reps` batches of `batch` launches between two
+        # events; the median batch over batch size.  (Timing one launch at a
+        # time with a host sync in between charges each short launch the
+        # GPU's idle gap and clock ramp: FLUX-512's 49 us forward reads
+        # about 70 us that way.)
+        t_w = time.perf_counter()
+        while time.perf_counter() - t_w < 0.25:
+            for _ in range(batch):
+                fn()
+            torch.cuda.synchronize()
         ts = []
         for _ in range(reps):
             e0, e1 = ev(), ev()
             e0.record(stream)
-            fn()
+            for _ in range(batch):
+                fn()
             e1.record(stream)
             torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
+            ts.append(e0.elapsed_time(e1) / batch)
         return statistics.median(ts)
 
     # the other bf16 workloads' attention, timed warm like the step (parity
@@ -473,41 +484,21 @@ def main():
 
     # Unified attention: FLUX-1024 on a 2 (Ulysses) x 4 (ring) mesh, every
     # device's share on this GPU (seq2head, a fused ring share per head group,
-    # head2seq), timed warm like the step
+    # head2seq), timed back to back like the other legs
     Pu, Pr = 2, 4
     usp_ws = torch.empty(cru.usp_workspace_bytes(q, Pu, Pr), dtype=torch.uint8, device=dev)
     o_usp = torch.empty_like(q)
     l_usp = torch.empty(B, H, S, dtype=torch.float32, device=dev)
     run_usp = lambda: cru.usp_emulate(q, k, v, Pu, Pr, fused=True, out=o_usp, lse=l_usp,
                                       workspace=usp_ws)
-    for _ in range(3):
-        run_usp()
-    ts = []
-    for _ in range(20):
-        e0, e1 = ev(), ev()
-        e0.record(stream)
-        run_usp()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1))
-    usp_ms = statistics.median(ts)
+    usp_ms = warm(run_usp)
     usp = {"workload": f"flux-1024, ulysses {Pu} x ring {Pr}, all devices' shares, fused ring",
            "ms_median": usp_ms, "TFLOP/s": f_full / (usp_ms * 1e-3) / 1e12}
 
     # the step's ring share with partials kept in bf16 (convert_to_fp32 off)
     run_rb = lambda: cru.ring_emulate(q_share, k, v, N, fused=True, convert_to_fp32=False,
                                       out=o_ring, lse=l_ring, workspace=ws)
-    for _ in range(3):
-        run_rb()
-    ts = []
-    for _ in range(20):
-        e0, e1 = ev(), ev()
-        e0.record(stream)
-        run_rb()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1))
-    rb_ms = statistics.median(ts)
+    rb_ms = warm(run_rb)
     ring_bf16 = {"workload": "flux-1024 ring rank-0 share (576 rows x 8 chunks), bf16 partials",
                  "ms_median": rb_ms, "TFLOP/s": f_ring / (rb_ms * 1e-3) / 1e12,
                  "fp32_partials_ms_in_step": part_ms["ring_share"]}
