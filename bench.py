@@ -163,9 +163,9 @@ def attn_only(n, heads=0):
 
 
 def load_sweep():
-    """The S=4608, D=128 forward at several head counts: time per workgroup
-    key tile as the number of busy CUs grows (18 workgroups of 256 query
-    rows per head; 256 CUs)."""
+    """The S=4608, D=128 forward at several head counts: throughput as the
+    number of busy CUs grows (4608 rows make 18 tiles of 256 rows per head;
+    the launch picks its own workgroup shape, 8 waves from 14 heads up)."""
     import torch
     import context_ring_ulysses_amd as cru
     S, D = 4608, 128
@@ -177,23 +177,21 @@ def load_sweep():
         v = torch.randn(1, S, H, D, device="cuda", generator=g).to(torch.bfloat16)
         o = torch.empty_like(q)
         l = torch.empty(1, H, S, device="cuda")
-        for _ in range(5):
-            cru.attn_fwd_lse(q, k, v, out=o, lse=l)
-        ts = []
-        for _ in range(50):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            cru.attn_fwd_lse(q, k, v, out=o, lse=l)
-            e1.record()
+        t_w = time.perf_counter()
+        while time.perf_counter() - t_w < 0.5:
+            for _ in range(10):
+                cru.attn_fwd_lse(q, k, v, out=o, lse=l)
             torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        t = statistics.median(ts)
-        wgs = 18 * H
-        rounds = -(-wgs // 256)
-        rows.append({"heads": H, "workgroups": wgs, "ms_median": t,
-                     "TFLOP/s": attn_flops(1, H, S, S, D) / (t * 1e-3) / 1e12,
-                     "us_per_workgroup_tile": t * 1e3 / rounds / (S // 64)})
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(51)]
+        evs[0].record()
+        for i in range(50):
+            cru.attn_fwd_lse(q, k, v, out=o, lse=l)
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        t = statistics.median(evs[i].elapsed_time(evs[i + 1]) for i in range(50))
+        tiles = 18 * H
+        rows.append({"heads": H, "row_tiles_of_256": tiles, "ms_median": t,
+                     "TFLOP/s": attn_flops(1, H, S, S, D) / (t * 1e-3) / 1e12})
         log(f"[bench] load sweep H={H}: {rows[-1]}")
     print(json.dumps({"load_sweep": rows}))
 
