@@ -60,20 +60,24 @@
 // The running max m is kept in log2 units (scores times scale*log2(e)), so
 // P = 2^(x - m) is one FMA and one v_exp_f32 per score.  Rescaling is lazy
 // and the tile max is not computed on the common path: tile t is
-// exponentiated against the current m, and only if some half-row's sum of
-// the tile's P passes kSumCap = 2^32 (the sum bounds every P of the tile, an
-// overflow to inf included) does the wave take the rare path that finds
-// the tile max, moves m there and exponentiates the tile again.  Any m gives
+// exponentiated against the current m, and only if some half-row's running
+// sum of P, this tile's included, passes kSumCap = 2^32 (the sum bounds
+// every P of the tile, an overflow to inf included) does the wave take the
+// rare path that finds the tile max, moves m there (and past the log2 of
+// the row's sum so far) and exponentiates the tile again.  Any m gives
 // the same O and LSE up to rounding (fp32 and bf16 keep their relative
-// precision at any scale below overflow); the cap only keeps P, l and O far
-// from the fp32 limit.  The first tile sets m to its own max.  The
-// 64-register rescale of O that a move owes is settled at the start of the
-// next tile, ahead of its QK^T block, so its branch never splits the block
-// the compiler interleaves (QK^T, exponentials, P V of the previous tile).
+// precision at any scale below overflow); the cap keeps P, l and O from the
+// fp32 limit: a half-row's sum stays below 2^32 between moves, so O's
+// accumulator (both halves, about 2^33 max|V|) is finite for max|V| < 2^90.
+// The first tile sets m to its own max.  The 64-register rescale of O that
+// a move owes is settled at the start of the next tile, ahead of its QK^T
+// block, so its branch never splits the block the compiler interleaves
+// (QK^T, exponentials, P V of the previous tile).
 // P is rounded to bf16 for the P V product, and O is normalised by the sum
-// of those same rounded values, so O's weights sum to one and a row that one
-// key dominates keeps that key's rounding out of O.  The LSE takes the sum
-// of the fp32 P, which the rounding would otherwise bias by up to 2^-9.
+// of those same rounded values (taken by the matrix cores beside O), so O's
+// weights sum to one and a row that one key dominates keeps that key's
+// rounding out of O.  The LSE takes the sum of the fp32 P, which the
+// rounding would otherwise bias by up to 2^-9.
 #include "attn_shape.h"
 #include "cru_kernels.h"
 

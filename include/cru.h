@@ -120,7 +120,9 @@ typedef struct {
  * to bf16 (nearest even) before the P V product, O is divided by the sum of
  * those rounded values (the LSE is taken from the sum of the unrounded
  * ones), and O is rounded to nearest even when o is bf16.  fp32 inputs run
- * in fp32 throughout.
+ * in fp32 throughout.  The bf16 path moves its running max lazily: a row's
+ * unnormalised sums may reach about 2^33 before the max moves, so O's fp32
+ * accumulator stays finite for max|V| below 2^90 (bf16 reaches 2^128).
  * Skv = 0 gives O = 0 and LSE = -inf; Sq = 0 enqueues nothing.
  * o must not overlap q, k or v.
  * Defined by: diffusers "Attention backends" page, "Available backends"

@@ -393,6 +393,36 @@ def test_extreme_logit_ranges(scale_to):
     assert err(to_f64(l), l_ref) <= TOL_LSE + D * 2.0 ** -24 * 300.0
 
 
+@pytest.mark.parametrize("vscale_log2", [80, 90])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_large_v_near_the_sum_cap(vscale_log2, out_dtype):
+    # The running max moves only when a half-row's running sum of P would
+    # pass 2^32, so O's accumulator can reach about 2^33 * max|V|.  Here the
+    # first key tile has logits near 0 and every later key about 17.5: tiles
+    # 1 and 2 add about 2^30.9 each to a half-row's sum without a move (the
+    # logits fix that sum: 32 keys of 2^(17.5 log2 e - m) each), tile 3
+    # forces one.  With V scaled
+    # by 2^90 (exact in bf16, max|V| about 2^92) the accumulator reaches
+    # about 2^125, below the fp32 limit; O / 2^s must match the oracle.
+    g = torch.Generator().manual_seed(15)
+    B, Sq, Skv, H, D = 1, 40, 640, 2, 128
+    q1 = torch.randn(B, 1, H, D, generator=g)
+    q1 = q1 / q1.norm(dim=-1, keepdim=True)
+    q = q1.expand(B, Sq, H, D).contiguous() + 0.01 * torch.randn(B, Sq, H, D, generator=g)
+    k = torch.randn(B, Skv, H, D, generator=g) * 0.01
+    k[:, 64:] += q1 * (17.5 * math.sqrt(D))
+    v = torch.randn(B, Skv, H, D, generator=g) * 2.0 ** vscale_log2
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    o, l = cru.attn_fwd_lse(*cuda(q, k, v), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all().item() and torch.isfinite(l).all().item()
+    o_ref, l_ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v) / 2.0 ** vscale_log2)
+    assert err(to_f64(o) / 2.0 ** vscale_log2, o_ref) <= TOL_O
+    # logits reach about 17.5 (plus a bf16 rounding of q and k): the fp32
+    # score sum rounds by at most D * 2^-24 * 18, which the LSE inherits
+    assert err(to_f64(l), l_ref) <= TOL_LSE
+
+
 def test_dominant_last_key_in_ragged_tile():
     # one key, the last of a ragged final tile, outweighs all others by e^40
     g = torch.Generator().manual_seed(14)
