@@ -27,6 +27,7 @@ kernels, and the fp64 oracle timed on the host cores.
     python bench.py --attn-only N        # N FLUX-1024 forwards only, for counters
     python bench.py --attn-only N --heads H   # the same shape with H heads
     python bench.py --load-sweep         # FLUX-1024-shaped forward at 1..48 heads
+    python bench.py --ceilings           # library GEMM, copy and read rates, for context
 """
 from __future__ import annotations
 
@@ -162,6 +163,52 @@ def attn_only(n, heads=0):
     log(f"[bench] {n} forwards done, {q.shape[2]} heads")
 
 
+def ceilings():
+    """What this GPU reaches on plain library work, beside the published
+    peaks the bars use: a dense bf16 GEMM through torch (hipBLASLt), a 1 GiB
+    device copy (read + write) and a 1 GiB read (a sum), each back to back
+    after a settling half second; the median of 20."""
+    import torch
+    dev = torch.device("cuda:0")
+
+    def timed(fn, reps=20):
+        t_w = time.perf_counter()
+        while time.perf_counter() - t_w < 0.5:
+            fn()
+            torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        evs[0].record()
+        for i in range(reps):
+            fn()
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        return statistics.median(evs[i].elapsed_time(evs[i + 1]) for i in range(reps))
+
+    out = {}
+    n = 8192
+    g = torch.Generator(device=dev).manual_seed(0)
+    a = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
+    c = torch.empty(n, n, dtype=torch.bfloat16, device=dev)
+    t = timed(lambda: torch.mm(a, b, out=c))
+    out["bf16_gemm_8192"] = {"ms_median": t, "TFLOP/s": 2.0 * n ** 3 / (t * 1e-3) / 1e12,
+                             "frac_of_2500": 2.0 * n ** 3 / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    del a, b, c
+    nb = 1 << 30
+    x = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    t = timed(lambda: y.copy_(x))
+    out["copy_1GiB"] = {"ms_median": t, "GB/s": 2 * nb / (t * 1e-3) / 1e9,
+                        "frac_of_8000": 2 * nb / (t * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    t = timed(lambda: torch.sum(x, dim=0, out=sink))
+    out["read_1GiB"] = {"ms_median": t, "GB/s": nb / (t * 1e-3) / 1e9,
+                        "frac_of_8000": nb / (t * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    for k, v in out.items():
+        log(f"[bench] ceiling {k}: {v}")
+    print(json.dumps({"ceilings": out}))
+
+
 def load_sweep():
     """The S=4608, D=128 forward at several head counts: throughput as the
     number of busy CUs grows (4608 rows make 18 tiles of 256 rows per head;
@@ -205,6 +252,8 @@ def main():
     ap.add_argument("--attn-reps", type=int, default=100,
                     help="timed launches of the full forward for the roofline leg")
     ap.add_argument("--load-sweep", action="store_true")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="library GEMM, copy and read rates on this GPU, for context")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--attn-only", type=int, default=0, metavar="N",
@@ -230,6 +279,9 @@ def main():
         return
     if args.load_sweep:
         load_sweep()
+        return
+    if args.ceilings:
+        ceilings()
         return
 
     dev = torch.device("cuda:0")
