@@ -14,6 +14,12 @@ attention shape (B=1, H=24, S=4096+512=4608, D=128, bf16, synthetic inputs):
      those heads of the [B, S, H, D] output (the regrouping by token fused
      into the store; the standalone head2seq kernel is timed cold below).
 
+The parts are independent; the timed step runs parts 2 and 3 on a second
+stream (default priority) beside 4's seq2head, 1 and 4's attention on the
+first, so the memory-bound merge and the short ring launches fill CUs the
+full forward leaves idle.  A second pass with the parts one after another
+gives the per-part breakdown.
+
 Inputs (and the merge's partials) are resident in HBM before timing starts.
 ``value`` is the attention work of a step (4*B*H*Sq*Skv*D summed over parts
 1, 2 and 4) divided by the step time.  The JSON line also carries each
@@ -317,37 +323,68 @@ def main():
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    def step(marks=None):
+    # a second stream at the default priority for the step's memory-bound
+    # and short parts
+    side = torch.cuda.Stream()
+
+    def step_parts(marks):
+        """One step with the parts one after another on one stream, an event
+        between parts: the per-part breakdown."""
         m = marks
-        if m: m[0].record(stream)
+        m[0].record(stream)
         cru.attn_fwd_lse(q, k, v, out=o_full, lse=l_full)
-        if m: m[1].record(stream)
+        m[1].record(stream)
         cru.ring_emulate(q_share, k, v, N, fused=True, out=o_ring, lse=l_ring, workspace=ws)
-        if m: m[2].record(stream)
+        m[2].record(stream)
         cru.attn_merge_lse(parts_o, parts_l, out=o_merge, lse=l_merge)
-        if m: m[3].record(stream)
+        m[3].record(stream)
         cru.ulysses_seq2head([q, k, v], P, out=ys)
         # group 0's heads of the [B, S, H, D] output: a strided view the
         # epilogue stores into directly (head2seq of this group, fused)
         cru.attn_fwd_lse(ys[0][0], ys[1][0], ys[2][0], out=o_u[:, :, :Hp], lse=l_u)
-        if m: m[4].record(stream)
+        m[4].record(stream)
+
+    def step():
+        """One step as timed: the ring share and the merge on the second
+        stream, beside the Ulysses share's seq2head, the full forward and
+        the Ulysses share's attention on the first; the step ends when both
+        are done.  The parts are independent, so the memory-bound merge and
+        the short ring launches fill the CUs the full forward leaves idle in
+        its partial last round of workgroups.  Same results, bit for bit, as
+        the parts one after another."""
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            cru.ring_emulate(q_share, k, v, N, fused=True, out=o_ring, lse=l_ring, workspace=ws)
+            cru.attn_merge_lse(parts_o, parts_l, out=o_merge, lse=l_merge)
+        cru.ulysses_seq2head([q, k, v], P, out=ys)
+        cru.attn_fwd_lse(q, k, v, out=o_full, lse=l_full)
+        cru.attn_fwd_lse(ys[0][0], ys[1][0], ys[2][0], out=o_u[:, :, :Hp], lse=l_u)
+        stream.wait_stream(side)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    marks = [[ev() for _ in range(5)] for _ in range(args.steps)]
     t_start, t_end = ev(), ev()
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        step(marks[i])
+        step()
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+
+    # the same step with its parts one after another on one stream, for the
+    # breakdown (and the step time without the overlap)
+    marks = [[ev() for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step_parts(marks[i])
+    torch.cuda.synchronize()
     part_ms = {name: statistics.mean(m[j].elapsed_time(m[j + 1]) for m in marks)
                for j, name in enumerate(["attn_full", "ring_share", "merge_all_rows", "ulysses_share"])}
+    ms_per_step_seq = statistics.mean(m[0].elapsed_time(m[4]) for m in marks)
 
     f_full = attn_flops(B, H, S, S, D)
     f_ring = attn_flops(B, H, b0 - a0, S, D)
@@ -357,7 +394,8 @@ def main():
     attn_tflops = f_full / (part_ms["attn_full"] * 1e-3) / 1e12
     mbytes = merge_bytes(N, B, S, H, D)
     merge_gbs = mbytes / (part_ms["merge_all_rows"] * 1e-3) / 1e9
-    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step; attn {part_ms['attn_full']:.3f} ms "
+    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (parts one after another: "
+        f"{ms_per_step_seq:.3f} ms); attn {part_ms['attn_full']:.3f} ms "
         f"= {attn_tflops:.1f} TFLOP/s; merge {merge_gbs:.0f} GB/s")
 
     # cold-cache bandwidth: reading 1 GiB between reps evicts L2 and the MALL
@@ -501,11 +539,13 @@ def main():
            for _ in range(3)]
     og2 = torch.zeros(P2, w2.B, w2.S, w2.H // P2, w2.D, dtype=q2.dtype, device=dev)
     lu2 = torch.empty(w2.B, w2.H // P2, w2.S, dtype=torch.float32, device=dev)
+    Hp2 = w2.H // P2
 
     def uly2():
+        # as in the step: the share's attention stores straight into its
+        # heads of the [B, S, H, D] output (head2seq fused into the store)
         cru.ulysses_seq2head([q2, k2, v2], P2, out=ys2)
-        cru.attn_fwd_lse(ys2[0][0], ys2[1][0], ys2[2][0], out=og2[0], lse=lu2)
-        cru.ulysses_head2seq(og2, P2, out=o2)
+        cru.attn_fwd_lse(ys2[0][0], ys2[1][0], ys2[2][0], out=o2[:, :, :Hp2], lse=lu2)
 
     t2_u = warm(uly2)
     t2b = q2.numel() * q2.element_size()
@@ -515,8 +555,8 @@ def main():
         "flux-512": {
             "workload": "flux-512 (B=1, S=1536, H=24, D=128, bf16)",
             "full_forward": {"ms_median": t2_full, "TFLOP/s": f2 / (t2_full * 1e-3) / 1e12},
-            "ulysses_share_incl_layouts": {"P": P2, "ms_median": t2_u,
-                                           "TFLOP/s": f2 / P2 / (t2_u * 1e-3) / 1e12},
+            "ulysses_share_incl_seq2head": {"P": P2, "ms_median": t2_u,
+                                            "TFLOP/s": f2 / P2 / (t2_u * 1e-3) / 1e12},
             "cold_layouts": {"note": "9.4 MB per tensor: launch-bound, and cache-resident "
                                      "in a real step",
                              "seq2head_qkv_GB/s": 6 * t2b / (m2s * 1e-3) / 1e9,
@@ -583,8 +623,10 @@ def main():
                    "ring_degree": N, "ulysses_degree": P,
                    "step": "full forward + ring rank-0 share (8 chunks, one split-KV launch) + "
                            "8-way merge over all rows + Ulysses rank-0 share (P=2, output "
-                           "stored straight into its heads of [B, S, H, D])",
+                           "stored straight into its heads of [B, S, H, D]); the ring share "
+                           "and the merge on a second stream beside the rest",
                    "step_attention_flops": step_flops},
+        "ms_per_step_parts_in_sequence": ms_per_step_seq,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "usp": usp,
@@ -592,7 +634,7 @@ def main():
         "cold_merge_bf16_partials": cold_merge_bf16,
         "other_workloads": other,
         "ulysses_anything_cold_layout": anything_layout,
-        "parts_ms": part_ms,
+        "parts_ms": part_ms,   # from the steps with the parts in sequence
         "attn_full_tflops": attn_tflops,
         "attn_full_frac_bf16_peak": attn_tflops / PEAK_BF16_TFLOPS,
         "ring_share_tflops": f_ring / (part_ms["ring_share"] * 1e-3) / 1e12,
