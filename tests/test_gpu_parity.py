@@ -968,6 +968,47 @@ def test_graph_capture_replays_match_eager():
     assert torch.equal(ref["x"], q)
 
 
+def test_calls_on_two_streams_match_one_stream():
+    # the library keeps no state between calls (outside the no-allocation
+    # entry point's scratch), so independent calls on two streams at the
+    # default priority, running at the same time, give the results the same
+    # calls give one after another, bit for bit
+    q, k, v = (t.cuda() for t in random_qkv(21, 1, 1200, 1200, 6, 128, gain=1.7))
+    qs = q[:, :300]
+    ws = torch.empty(cru.ring_workspace_bytes(qs, 4), dtype=torch.uint8, device="cuda")
+    parts_o = [torch.randn(1, 1200, 6, 128, device="cuda") for _ in range(5)]
+    parts_l = [torch.randn(1, 6, 1200, device="cuda") for _ in range(5)]
+    outs = [torch.empty_like(q), torch.empty(1, 6, 1200, device="cuda"),
+            torch.empty_like(qs), torch.empty(1, 6, 300, device="cuda"),
+            torch.empty(1, 1200, 6, 128, dtype=torch.bfloat16, device="cuda"),
+            torch.empty(1, 6, 1200, device="cuda")]
+
+    def first():
+        cru.attn_fwd_lse(q, k, v, out=outs[0], lse=outs[1])
+
+    def second():
+        cru.ring_emulate(qs, k, v, 4, fused=True, out=outs[2], lse=outs[3], workspace=ws)
+        cru.attn_merge_lse(parts_o, parts_l, out=outs[4], lse=outs[5])
+
+    first()
+    second()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    for rep in range(3):
+        for t in outs:
+            t.fill_(5.0)
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            second()
+        first()
+        main.wait_stream(side)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, ref)):
+            assert torch.equal(a, b), (rep, i)
+
+
 def test_device_errors():
     q, k, v = random_qkv(14, 1, 16, 16, 2, 64)
     with pytest.raises(cru.CruDeviceError):
