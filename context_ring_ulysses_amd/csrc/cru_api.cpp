@@ -649,17 +649,17 @@ cru_status cru_ulysses_head2seq(int n, const void* const* y, const cru_tensor* x
 //   2. per head group u, the ring over ring_degree sequence chunks: every
 //      query row of the group against every chunk, fp32 partials folded in
 //      ascending chunk order (rows of chunk r are ring rank r's share);
-//   3. head2seq of the group outputs (the reverse all-to-all).
-// The workspace holds the three regrouped inputs, the regrouped output and
-// one ring workspace, reused by every group.
-static size_t usp_parts(const cru_tensor* q, int Pu, int Pr, size_t* y_bytes, size_t* og_bytes,
+//   3. the reverse all-to-all: each group's folded output is stored straight
+//      into its heads of o (head2seq fused into the fold's store).
+// The workspace holds the three regrouped inputs and one ring workspace,
+// reused by every group.
+static size_t usp_parts(const cru_tensor* q, int Pu, int Pr, size_t* y_bytes,
                         size_t* ring_bytes) {
   const size_t elems = (size_t)q->B * q->S * q->H * q->D;
   const size_t rows_g = (size_t)q->B * q->S * (q->H / Pu);
   *y_bytes = align256(elems * elem_bytes(q->dtype));
-  *og_bytes = align256(elems * 4);
   *ring_bytes = (size_t)Pr * (align256(rows_g * q->D * 4) + align256(rows_g * 4));
-  return 3 * *y_bytes + *og_bytes + *ring_bytes;
+  return 3 * *y_bytes + *ring_bytes;
 }
 
 static cru_status usp_degrees(const cru_tensor* q, int Pu, int Pr) {
@@ -682,8 +682,8 @@ cru_status cru_usp_workspace_bytes(const cru_tensor* q, int ulysses_degree, int 
   if (bytes == nullptr) return fail(CRU_EINVAL, "bytes is NULL");
   CRU_TRY(check_tensor(q, "q"));
   CRU_TRY(usp_degrees(q, ulysses_degree, ring_degree));
-  size_t y, og, ring;
-  *bytes = usp_parts(q, ulysses_degree, ring_degree, &y, &og, &ring);
+  size_t y, ring;
+  *bytes = usp_parts(q, ulysses_degree, ring_degree, &y, &ring);
   return CRU_OK;
 }
 
@@ -706,8 +706,8 @@ cru_status cru_usp_emulate(const cru_tensor* q, const cru_tensor* k, const cru_t
   CRU_TRY(usp_degrees(q, Pu, Pr));
   float scale_log2 = 0.0f;
   CRU_TRY(check_scale(scale, q->D, &scale_log2));
-  size_t y_bytes, og_bytes, ring_bytes;
-  const size_t need = usp_parts(q, Pu, Pr, &y_bytes, &og_bytes, &ring_bytes);
+  size_t y_bytes, ring_bytes;
+  const size_t need = usp_parts(q, Pu, Pr, &y_bytes, &ring_bytes);
   if (need > 0 && workspace == nullptr) return fail(CRU_EWORKSPACE, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(CRU_EWORKSPACE, "workspace is not 256-byte aligned");
@@ -718,8 +718,7 @@ cru_status cru_usp_emulate(const cru_tensor* q, const cru_tensor* k, const cru_t
   const int64_t B = q->B, S = q->S, H = q->H, D = q->D, Hp = H / Pu;
   char* ws = static_cast<char*>(workspace);
   void* y[3] = {ws, ws + y_bytes, ws + 2 * y_bytes};
-  char* og = ws + 3 * y_bytes;
-  void* ring_ws = og + og_bytes;
+  void* ring_ws = ws + 3 * y_bytes;
 
   const cru_tensor x3[3] = {*q, *k, *v};
   CRU_TRY(cru_ulysses_seq2head(3, x3, y, Pu, 0, stream));
@@ -734,20 +733,20 @@ cru_status cru_usp_emulate(const cru_tensor* q, const cru_tensor* k, const cru_t
       t[i].H = Hp;
       t[i].sb = S * Hp * D; t[i].ss = Hp * D; t[i].sh = D;
     }
-    cru_tensor og_u = t[0];
-    og_u.data = og + u * group * o_es;
-    og_u.dtype = o->dtype;
+    // the group's heads of o: the fold stores there directly
+    cru_tensor o_u = *o;
+    o_u.data = static_cast<char*>(o->data) + u * Hp * o->sh * o_es;
+    o_u.H = Hp;
     cru_lse lse_u;
     if (lse != nullptr) {
       lse_u = *lse;
       lse_u.data = lse->data + u * Hp * lse->sh;
       lse_u.H = Hp;
     }
-    CRU_TRY(cru_ring_emulate(&t[0], &t[1], &t[2], Pr, 0, nullptr, fused, convert_to_fp32, &og_u,
+    CRU_TRY(cru_ring_emulate(&t[0], &t[1], &t[2], Pr, 0, nullptr, fused, convert_to_fp32, &o_u,
                              lse ? &lse_u : nullptr, scale, ring_ws, ring_bytes, stream));
   }
-  const void* og_p[1] = {og};
-  return cru_ulysses_head2seq(1, og_p, o, Pu, 0, stream);
+  return CRU_OK;
 }
 
 }  // extern "C"

@@ -309,7 +309,7 @@ cru_status cru_ulysses_head2seq(int n, const void* const* y,
  * cru_usp_workspace_bytes -- bytes of device workspace cru_usp_emulate needs
  * for q's shape and the two degrees (the same size serves bf16 and fp32
  * outputs).  Same divisibility rules as cru_usp_emulate.  It holds the
- * regrouped q, k, v and output of the Ulysses all-to-all (diffusers "Context
+ * regrouped q, k, v of the Ulysses all-to-all (diffusers "Context
  * parallelism" guide, "Unified Attention" section) and one ring workspace of
  * fp32 partials (diffusers "Parallelism" API page, ContextParallelConfig,
  * convert_to_fp32).  Host-only; bytes is written on success.
@@ -327,7 +327,8 @@ cru_status cru_usp_workspace_bytes(const cru_tensor* q, int ulysses_degree,
  *      partials folded in ascending chunk order (the rows of chunk r are
  *      ring rank r's share; fused and convert_to_fp32 as in
  *      cru_ring_emulate);
- *   3. head2seq of the group outputs into o.
+ *   3. the reverse all-to-all: each group's result is stored straight into
+ *      its heads of o (head2seq fused into the fold's store).
  *
  *   q, k, v   [B, S, H, D] bf16 or fp32, one sequence (k and v have q's S)
  *   ulysses_degree >= 1 must divide H, and ulysses_degree * ring_degree

@@ -377,7 +377,9 @@ def test_usp_validation():
     a256 = lambda x: (x + 255) // 256 * 256
     elems = 1 * 16 * 4 * 64
     rows_g = 1 * 16 * 2
-    assert need.value == 3 * a256(elems * 2) + a256(elems * 4) + 2 * (a256(rows_g * 64 * 4) + a256(rows_g * 4))
+    # the three regrouped inputs and one ring workspace of fp32 partials (the
+    # groups' results are stored straight into o)
+    assert need.value == 3 * a256(elems * 2) + 2 * (a256(rows_g * 64 * 4) + a256(rows_g * 4))
     assert usp(q, q, q, 2, 2, ws_bytes=need.value - 1) == EWORKSPACE
     assert usp(q, q, q, 2, 2, ws_bytes=need.value) == EDEVICE
 
