@@ -134,7 +134,41 @@ def cpu_baseline(budget_s=10.0, max_forwards=480):
             "kind": "oracle", "cpu_model": cpu_model, "blas": blas,
             "host_cpus_visible": len(os.sched_getaffinity(0)),
             "sample": f"fp64 oracle full forward of FLUX-1024 (S=4608, D=128, all rows), "
-                      f"{done} single-head forwards (heads cycled), {spent:.1f} s"}
+                      f"{done} single-head forwards (heads cycled), {spent:.1f} s",
+            "per_config": cpu_per_config()}
+
+
+def cpu_per_config(budget_s=2.5):
+    """The oracle on the other bf16 workloads and on FLUX-1024's ring share
+    (its 576 rows against the 8 chunks, folded in order), one (batch, head)
+    at a time until about ``budget_s`` each; TFLOP/s with the GPU's flop
+    count.  Reported beside the headline baseline, not a target."""
+    import oracle
+    from workloads import make_inputs, to_f64, workload
+    out = {}
+
+    def run(name, idx, fn, flops_per_call):
+        w = workload(idx)
+        q, k, v = make_inputs(idx)
+        done, spent = 0, 0.0
+        while spent < budget_s:
+            b, h = (done // w.H) % w.B, done % w.H
+            qh, kh, vh = (to_f64(t[b:b + 1, :, h:h + 1]) for t in (q, k, v))
+            t0 = time.perf_counter()
+            fn(qh, kh, vh, w)
+            spent += time.perf_counter() - t0
+            done += 1
+        out[name] = {"TFLOP/s": done * flops_per_call(w) / spent / 1e12,
+                     "sample": f"{done} single-head calls, {spent:.1f} s"}
+
+    full = lambda qh, kh, vh, w: oracle.attention(qh, kh, vh)
+    run("flux-512 full forward", 2, full, lambda w: attn_flops(1, 1, w.S, w.S, w.D))
+    run("ring-anything-4645 full forward", 4, full, lambda w: attn_flops(1, 1, w.S, w.S, w.D))
+    run("video-dit-4276 full forward", 5, full, lambda w: attn_flops(1, 1, w.S, w.S, w.D))
+    run("flux-1024 ring rank-0 share (8 chunks, fold)", 3,
+        lambda qh, kh, vh, w: oracle.ring_share(qh, kh, vh, w.ring_degree, 0),
+        lambda w: attn_flops(1, 1, oracle.chunk_bounds(w.S, w.ring_degree)[0][1], w.S, w.D))
+    return out
 
 
 def copy_calibration():
