@@ -51,28 +51,33 @@
 // the iteration for tile t the waves compute S^T of tile t (K buffer t%2)
 // and the P V product of tile t-1 (V buffer (t-1)%2), while the loads of K of
 // tile t+1 and V of tile t fill the other two buffers.  One barrier per tile
-// separates them.  The P V product of tile t-1 does not depend on tile t, so
-// it keeps the matrix cores busy while the vector unit computes tile t's
-// exponentials.  Global loads go through buffer descriptors built per tile
+// separates them.  The softmax runs half a tile behind the scores, by 32-key
+// blocks: beside the QK^T of tile t each wave exponentiates the second block
+// of tile t-1 (whose S^T it kept), and beside the P V of tile t-1 the first
+// block of tile t.  So each of the two matrix phases has vector work of the
+// same wave to interleave with: the matrix cores overlap a wave's own vector
+// work, hardly the other wave's on the SIMD.  Global loads go through buffer descriptors built per tile
 // whose range ends at the last valid key row: rows past it read as zero
 // with no per-load bounds arithmetic.
 //
 // The running max m is kept in log2 units (scores times scale*log2(e)), so
 // P = 2^(x - m) is one FMA and one v_exp_f32 per score.  Rescaling is lazy
-// and the tile max is not computed on the common path: tile t is
+// and no max is computed on the common path: each 32-key block is
 // exponentiated against the current m, and only if some half-row's running
-// sum of P, this tile's included, passes kSumCap = 2^32 (the sum bounds
-// every P of the tile, an overflow to inf included) does the wave take the
-// rare path that finds the tile max, moves m there (and past the log2 of
-// the row's sum so far) and exponentiates the tile again.  Any m gives
+// sum of P, this block's included, passes kSumCap = 2^32 (the sum bounds
+// every P of the block, an overflow to inf included) does the wave take the
+// rare path that finds the block max, moves m there (and past the log2 of
+// the row's sum so far) and exponentiates the block again.  Any m gives
 // the same O and LSE up to rounding (fp32 and bf16 keep their relative
 // precision at any scale below overflow); the cap keeps P, l and O from the
 // fp32 limit: a half-row's sum stays below 2^32 between moves, so O's
 // accumulator (both halves, about 2^33 max|V|) is finite for max|V| < 2^90.
-// The first tile sets m to its own max.  The 64-register rescale of O that
-// a move owes is settled at the start of the next tile, ahead of its QK^T
-// block, so its branch never splits the block the compiler interleaves
-// (QK^T, exponentials, P V of the previous tile).
+// The first tile sets m to its own max.  A move at a tile's first block
+// comes after the P V of the tile before it was issued: the 64-register
+// rescale of O it owes is settled at the start of the next tile, ahead of
+// its QK^T, so the branch never splits a phase the compiler interleaves.  A
+// move at the previous tile's second block (beside QK^T) rescales O and that
+// tile's first-block P (already bf16, rounded again) before the P V.
 // P is rounded to bf16 for the P V product, and O is normalised by the sum
 // of those same rounded values (taken by the matrix cores beside O), so O's
 // weights sum to one and a row that one key dominates keeps that key's
@@ -293,180 +298,200 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
         s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[k], s[jb], 0, 0, 0);
       }
   };
-  // O^T += V^T P^T for the tile in vb
-  auto pv = [&](const char* vb, const bf16x8 (&pf)[T::NJ][2]) {
+  // P V for one 32-key block jb of the tile in vb (P^T of that block in pf)
+  auto pv_blk = [&](const char* vb, int jb, const bf16x8 (&pf)[2]) {
 #pragma unroll
-    for (int jb = 0; jb < T::NJ; ++jb)
+    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
+      for (int db = 0; db < T::ND; ++db) {
+        const int kb0 = (jb * 32 + hf * 16) * T::RB;
+        const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr(vb, kb0 + vread[db]));
+        const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr(vb, kb0 + 4 * T::RB + vread[db]));
+        const bf16x8 va = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[hf], oacc[db], 0, 0, 0);
+        if (db == T::ND - 1)
+          lbacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_pat, pf[hf], lbacc, 0, 0, 0);
+      }
+  };
+  // P = 2^(s*scale*log2e - m) for one 32-key block, rounded to bf16; lt
+  // sums the fp32 P (this half-lane's share)
+  auto exps_blk = [&](const f32x16& sblk, float mref, float& lt, bf16x8 (&pb)[2]) {
+    lt = 0.0f;
 #pragma unroll
-        for (int db = 0; db < T::ND; ++db) {
-          const int kb0 = (jb * 32 + hf * 16) * T::RB;
-          // keys +0..3 and +4..7 of the 8 this lane contributes; joined as
-          // whole 64-bit words (no per-element conversion)
-          const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr(vb, kb0 + vread[db]));
-          const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr(vb, kb0 + 4 * T::RB + vread[db]));
-          const bf16x8 va = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[jb][hf], oacc[db], 0, 0, 0);
-          if (db == T::ND - 1)
-            lbacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_pat, pf[jb][hf], lbacc, 0, 0, 0);
-        }
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int t2 = 0; t2 < 4; ++t2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sblk[hf * 8 + 2 * t2], a.scale_log2, -mref));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sblk[hf * 8 + 2 * t2 + 1], a.scale_log2, -mref));
+        lt += p0;
+        lt += p1;
+        const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+        pb[hf][2 * t2] = pp[0];
+        pb[hf][2 * t2 + 1] = pp[1];
+      }
+  };
+  auto blk_max = [&](const f32x16& sblk) {
+    float mx = sblk[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sblk[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    return mx * a.scale_log2;
+  };
+  auto rescale_o = [&](float alpha) {
+#pragma unroll
+    for (int db = 0; db < T::ND; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    lbacc *= alpha;
+  };
+  // rare path: a block's running sum passed the cap; move m past the block's
+  // max and past log2 of the row's sum so far (every P relative to the new m
+  // is at most 1) and return the factor the earlier sums scale by
+  auto move_max = [&](const f32x16& sblk) {
+    const float lrow = l + __shfl_xor(l, 32);
+    const float mn = fmaxf(fmaxf(m, blk_max(sblk)), m + __builtin_amdgcn_logf(lrow));
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    l *= alpha;
+    m = mn;
+    return alpha;
   };
 
-  // One tile t: start the loads of K (tile t+1) and V (tile t), S^T of tile
-  // t, its softmax, and the P V product of tile t-1 (whose P is p_prev).
-  // Out-of-range tiles read as zero through their descriptors, so the body
-  // has no per-tile conditions; the last tile is a separate instance that
-  // masks the keys past the end of the range.
-  auto step = [&](const char* kb_t, char* kb_n, char* vb_t, const char* vb_p,
-                  const bf16x8 (&p_prev)[T::NJ][2], bf16x8 (&p_new)[T::NJ][2], int t,
+  // Carried between steps: S^T of the previous tile's second 32-key block
+  // (its exponentials run beside this step's QK^T) and P of the previous
+  // tile's first block (computed beside the previous step's P V).
+  f32x16 sb1;
+  bf16x8 p0_prev[2];
+
+  // One tile t: start the loads of K (tile t+1) and V (tile t); S^T of tile
+  // t beside the exponentials of tile t-1's second block; then P V of tile
+  // t-1 beside the exponentials of tile t's first block.  Each matrix phase
+  // has vector work of its own wave to interleave with.
+  auto step = [&](const char* kb_t, char* kb_n, char* vb_t, const char* vb_p, int t,
                   auto first_tag, auto last_tag) {
     constexpr bool kFirst = decltype(first_tag)::value;
     constexpr bool kLastTile = decltype(last_tag)::value;
     __syncthreads();            // tile t's K and tile t-1's V are in; kb_n, vb_t are free
     dma(kb_n, kg, a.k_ss, t + 1, koff);
     dma(vb_t, vg, a.v_ss, t, voff);
-    // O holds tiles up to t-2 relative to the max before tile t-1's move;
-    // settle that rescale (rare: only when the max moved) before tile t-1 is
-    // added below.  Settling here, ahead of the QK^T block, keeps its branch
-    // out of the block so the compiler can interleave the whole tile.
     if constexpr (!kFirst) {
-      if (owed) {
-#pragma unroll
-        for (int db = 0; db < T::ND; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha_owed;
-        lbacc *= alpha_owed;
-      }
+      if (owed) rescale_o(alpha_owed);   // a move in the previous step's second phase
     }
-
     f32x16 sc[T::NJ];
-    // S^T of tile t; keys past the end of the range (last tile) do not exist
-    auto scores = [&]() {
-      qk(kb_t, sc);
-      if constexpr (kLastTile) {
-        const int valid = nkv - t * T::BC;
-#pragma unroll
-        for (int jb = 0; jb < T::NJ; ++jb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = jb * 32 + 16 * (r >> 3) + 8 * lh + (r & 7);
-            if (key >= valid) sc[jb][r] = -__builtin_inff();
-          }
-      }
-    };
-    scores();
-
-    // P = 2^(s*scale*log2e - m), rounded to bf16 (nearest even) for the
-    // P V product (whose row sum the matrix cores take beside it, for O's
-    // normaliser).  lt sums the fp32 P for the LSE: this half-lane's share
-    // of the tile's sum.
-    auto exps = [&](float mref, float& lt) {
-      lt = 0.0f;
+    qk(kb_t, sc);
+    if constexpr (kLastTile) {
+      const int valid = nkv - t * T::BC;
 #pragma unroll
       for (int jb = 0; jb < T::NJ; ++jb)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-          for (int t2 = 0; t2 < 4; ++t2) {
-            const float p0 = __builtin_amdgcn_exp2f(
-                __builtin_fmaf(sc[jb][hf * 8 + 2 * t2], a.scale_log2, -mref));
-            const float p1 = __builtin_amdgcn_exp2f(
-                __builtin_fmaf(sc[jb][hf * 8 + 2 * t2 + 1], a.scale_log2, -mref));
-            lt += p0;
-            lt += p1;
-            const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
-            p_new[jb][hf][2 * t2] = pp[0];
-            p_new[jb][hf][2 * t2 + 1] = pp[1];
-          }
-    };
-    // max of this row's scores in the tile (both halves), in log2 units
-    auto tile_max = [&]() {
+        for (int r = 0; r < 16; ++r) {
+          const int key = jb * 32 + 16 * (r >> 3) + 8 * lh + (r & 7);
+          if (key >= valid) sc[jb][r] = -__builtin_inff();
+        }
+    }
+    if constexpr (kFirst) {
+      // O and l are empty: m starts at the tile's own max (both blocks)
       float mx = sc[0][0];
 #pragma unroll
       for (int jb = 0; jb < T::NJ; ++jb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[jb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      return mx * a.scale_log2;
-    };
-
-    if constexpr (kFirst) {
-      // O and l are empty: start from the tile's own max, nothing is owed
-      m = tile_max();
-      exps(m, l);
+      m = mx * a.scale_log2;
+      float lt0;
+      exps_blk(sc[0], m, lt0, p0_prev);
+      l = lt0;
       owed = false;
     } else {
-      float lt;
-      exps(m, lt);
-      // tile t-1, whose P is relative to m before this tile
-      pv(vb_p, p_prev);
-      // rare: the running sum with this tile's P passes the cap (a P of
-      // this tile overflowing to inf included)
-      const bool move = __ballot(l + lt > kSumCap) != 0ull;
-      if (move) {
-        // S^T is recomputed from the K tile (still in LDS until the next
-        // barrier) rather than kept live across the P V block
-        asm volatile("" ::: "memory");
-        scores();
-        // the new max covers this tile's scores and, through log2 of the
-        // row's running sum (the LSE so far, in log2 units, which is at
-        // least the max of every earlier score), the earlier tiles: every P
-        // relative to it is at most 1
-        const float lrow = l + __shfl_xor(l, 32);
-        const float mn = fmaxf(fmaxf(m, tile_max()), m + __builtin_amdgcn_logf(lrow));
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);
-        l *= alpha;
-        m = mn;
-        alpha_owed = alpha;
-        exps(m, lt);
+      // tile t-1's second block, beside this tile's QK^T
+      bf16x8 p1[2];
+      float lt1;
+      exps_blk(sb1, m, lt1, p1);
+      if (__ballot(l + lt1 > kSumCap) != 0ull) {
+        const float alpha = move_max(sb1);
+        exps_blk(sb1, m, lt1, p1);
+        // O (tiles up to t-2) and tile t-1's first block were relative to
+        // the old max (rare path)
+        rescale_o(alpha);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const float x0 = (float)p0_prev[hf][e] * alpha, x1 = (float)p0_prev[hf][e + 1] * alpha;
+            const bf16x2 pp = {(__bf16)x0, (__bf16)x1};
+            p0_prev[hf][e] = pp[0];
+            p0_prev[hf][e + 1] = pp[1];
+          }
       }
-      // tiles up to t-1 are now in O relative to m before this tile's move
-      owed = move;
-      l += lt;
+      l += lt1;
+      // P V of tile t-1, beside this tile's first-block exponentials
+      pv_blk(vb_p, 0, p0_prev);
+      pv_blk(vb_p, 1, p1);
+      bf16x8 p0n[2];
+      float lt0;
+      exps_blk(sc[0], m, lt0, p0n);
+      const bool move = __ballot(l + lt0 > kSumCap) != 0ull;
+      if (move) {
+        asm volatile("" ::: "memory");
+        alpha_owed = move_max(sc[0]);
+        exps_blk(sc[0], m, lt0, p0n);
+      }
+      owed = move;   // O now holds tile t-1 relative to the max before this move
+      l += lt0;
+      p0_prev[0] = p0n[0];
+      p0_prev[1] = p0n[1];
     }
-
+    sb1 = sc[1];
     // this wave's loads must land before the next barrier publishes them
     __builtin_amdgcn_s_waitcnt(kWaitVmem);
   };
 
-  auto settle = [&]() {
-    if (owed) {
+  // after the last step: tile T-1's second block and its P V (V in vb)
+  auto finish = [&](const char* vb) {
+    __syncthreads();
+    if (owed) rescale_o(alpha_owed);
+    bf16x8 p1[2];
+    float lt1;
+    exps_blk(sb1, m, lt1, p1);
+    if (__ballot(l + lt1 > kSumCap) != 0ull) {
+      const float alpha = move_max(sb1);
+      exps_blk(sb1, m, lt1, p1);
+      rescale_o(alpha);
 #pragma unroll
-      for (int db = 0; db < T::ND; ++db)
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha_owed;
-      lbacc *= alpha_owed;
+        for (int e = 0; e < 8; e += 2) {
+          const float x0 = (float)p0_prev[hf][e] * alpha, x1 = (float)p0_prev[hf][e + 1] * alpha;
+          const bf16x2 pp = {(__bf16)x0, (__bf16)x1};
+          p0_prev[hf][e] = pp[0];
+          p0_prev[hf][e + 1] = pp[1];
+        }
     }
+    l += lt1;
+    pv_blk(vb, 0, p0_prev);
+    pv_blk(vb, 1, p1);
   };
 
   if (ntiles > 0) {
     dma(kbuf0, kg, a.k_ss, 0, koff);
     __builtin_amdgcn_s_waitcnt(kWaitVmem);
-    bf16x8 pa[T::NJ][2], pb[T::NJ][2];
     // Tiles come in (odd, even) pairs after tile 0; buffers alternate by parity.
     if (ntiles == 1) {
-      step(kbuf0, kbuf1, vbuf0, vbuf1, pb, pa, 0, First{}, Last{});
-      __syncthreads();
-      pv(vbuf0, pa);            // nothing owed after tile 0
+      step(kbuf0, kbuf1, vbuf0, vbuf1, 0, First{}, Last{});
+      finish(vbuf0);
     } else {
-      step(kbuf0, kbuf1, vbuf0, vbuf1, pb, pa, 0, First{}, NotLast{});
+      step(kbuf0, kbuf1, vbuf0, vbuf1, 0, First{}, NotLast{});
       int t = 1;
       for (; t + 2 < ntiles; t += 2) {
-        step(kbuf1, kbuf0, vbuf1, vbuf0, pa, pb, t, NotFirst{}, NotLast{});
-        step(kbuf0, kbuf1, vbuf0, vbuf1, pb, pa, t + 1, NotFirst{}, NotLast{});
+        step(kbuf1, kbuf0, vbuf1, vbuf0, t, NotFirst{}, NotLast{});
+        step(kbuf0, kbuf1, vbuf0, vbuf1, t + 1, NotFirst{}, NotLast{});
       }
       if (t + 1 < ntiles) {       // two left: t odd, t+1 even and last
-        step(kbuf1, kbuf0, vbuf1, vbuf0, pa, pb, t, NotFirst{}, NotLast{});
-        step(kbuf0, kbuf1, vbuf0, vbuf1, pb, pa, t + 1, NotFirst{}, Last{});
-        __syncthreads();
-        settle();
-        pv(vbuf0, pa);
+        step(kbuf1, kbuf0, vbuf1, vbuf0, t, NotFirst{}, NotLast{});
+        step(kbuf0, kbuf1, vbuf0, vbuf1, t + 1, NotFirst{}, Last{});
+        finish(vbuf0);
       } else {                    // one left: t odd and last
-        step(kbuf1, kbuf0, vbuf1, vbuf0, pa, pb, t, NotFirst{}, Last{});
-        __syncthreads();
-        settle();
-        pv(vbuf1, pb);
+        step(kbuf1, kbuf0, vbuf1, vbuf0, t, NotFirst{}, Last{});
+        finish(vbuf1);
       }
     }
   }
