@@ -132,8 +132,9 @@ struct Tile {
 
 struct NotFirst { static constexpr bool value = false; };
 struct First { static constexpr bool value = true; };
-struct NotLast { static constexpr bool value = false; };
-struct Last { static constexpr bool value = true; };
+struct NotLast { static constexpr int value = 0; };
+struct Last { static constexpr int value = 1; };
+struct MaybeLast { static constexpr int value = 2; };   // decided at run time
 
 __device__ __forceinline__ int key_row(int j) {
   // swap bits 2 and 3 of the key index (an involution)
@@ -369,7 +370,7 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
   auto step = [&](const char* kb_t, char* kb_n, char* vb_t, const char* vb_p, int t,
                   auto first_tag, auto last_tag) {
     constexpr bool kFirst = decltype(first_tag)::value;
-    constexpr bool kLastTile = decltype(last_tag)::value;
+    constexpr int kLast = decltype(last_tag)::value;
     __syncthreads();            // tile t's K and tile t-1's V are in; kb_n, vb_t are free
     dma(kb_n, kg, a.k_ss, t + 1, koff);
     dma(vb_t, vg, a.v_ss, t, voff);
@@ -378,7 +379,8 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
     }
     f32x16 sc[T::NJ];
     qk(kb_t, sc);
-    if constexpr (kLastTile) {
+    // keys past the end of the range (in the last tile) do not exist
+    auto mask = [&]() {
       const int valid = nkv - t * T::BC;
 #pragma unroll
       for (int jb = 0; jb < T::NJ; ++jb)
@@ -387,6 +389,11 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
           const int key = jb * 32 + 16 * (r >> 3) + 8 * lh + (r & 7);
           if (key >= valid) sc[jb][r] = -__builtin_inff();
         }
+    };
+    if constexpr (kLast == 1) {
+      mask();
+    } else if constexpr (kLast == 2) {
+      if (t == ntiles - 1) mask();   // uniform: the whole workgroup agrees
     }
     if constexpr (kFirst) {
       // O and l are empty: m starts at the tile's own max (both blocks)
@@ -474,25 +481,22 @@ attn_fwd_bf16_kernel(const AttnArgs a) {
   if (ntiles > 0) {
     dma(kbuf0, kg, a.k_ss, 0, koff);
     __builtin_amdgcn_s_waitcnt(kWaitVmem);
-    // Tiles come in (odd, even) pairs after tile 0; buffers alternate by parity.
-    if (ntiles == 1) {
-      step(kbuf0, kbuf1, vbuf0, vbuf1, 0, First{}, Last{});
+    // Tiles come in (odd, even) pairs after tile 0; buffers alternate by
+    // parity.  The last tile masks its keys past the end: an even last tile
+    // is the second step of a pair (a uniform branch there), an odd one the
+    // step after the loop.  Few step instances keep the code, and the
+    // registers the compiler assigns across them, small.
+    step(kbuf0, kbuf1, vbuf0, vbuf1, 0, First{}, MaybeLast{});
+    int t = 1;
+    for (; t + 1 < ntiles; t += 2) {
+      step(kbuf1, kbuf0, vbuf1, vbuf0, t, NotFirst{}, NotLast{});
+      step(kbuf0, kbuf1, vbuf0, vbuf1, t + 1, NotFirst{}, MaybeLast{});
+    }
+    if (t < ntiles) {             // t odd and last
+      step(kbuf1, kbuf0, vbuf1, vbuf0, t, NotFirst{}, Last{});
+      finish(vbuf1);
+    } else {                      // the last tile was even
       finish(vbuf0);
-    } else {
-      step(kbuf0, kbuf1, vbuf0, vbuf1, 0, First{}, NotLast{});
-      int t = 1;
-      for (; t + 2 < ntiles; t += 2) {
-        step(kbuf1, kbuf0, vbuf1, vbuf0, t, NotFirst{}, NotLast{});
-        step(kbuf0, kbuf1, vbuf0, vbuf1, t + 1, NotFirst{}, NotLast{});
-      }
-      if (t + 1 < ntiles) {       // two left: t odd, t+1 even and last
-        step(kbuf1, kbuf0, vbuf1, vbuf0, t, NotFirst{}, NotLast{});
-        step(kbuf0, kbuf1, vbuf0, vbuf1, t + 1, NotFirst{}, Last{});
-        finish(vbuf0);
-      } else {                    // one left: t odd and last
-        step(kbuf1, kbuf0, vbuf1, vbuf0, t, NotFirst{}, Last{});
-        finish(vbuf1);
-      }
     }
   }
 
