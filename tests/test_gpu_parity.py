@@ -78,23 +78,6 @@ def check_all(o_gpu, l_gpu, o_ref, l_ref, tol_o, tol_l, what):
     assert el <= tol_l, f"{what}: LSE error {el}"
 
 
-def sample_rows(S, n=48, seed=0):
-    rng = np.random.default_rng(seed)
-    fixed = [0, 1, 31, 32, 63, 64, 127, 128, 129, 255, 256, 257, S // 2, S - 2, S - 1]
-    rows = set(r for r in fixed if 0 <= r < S)
-    rows |= set(rng.choice(S, size=min(n, S), replace=False).tolist())
-    return np.array(sorted(rows))
-
-
-def check_rows(o_gpu, l_gpu, q64, k64, v64, rows, tol_o, tol_l, what):
-    o_ref, l_ref = oracle.attention(q64[:, rows], k64, v64)
-    eo = err(to_f64(o_gpu)[:, rows], o_ref)
-    el = err(to_f64(l_gpu)[:, :, rows], l_ref)
-    say(f"  {what}: max|dO| = {eo:.3e}, max|dLSE| = {el:.3e} over {len(rows)} rows")
-    assert eo <= tol_o, f"{what}: O error {eo}"
-    assert el <= tol_l, f"{what}: LSE error {el}"
-
-
 # ------------------------------------------------------------ fp32 (workload 1)
 
 def test_fp32_tiny_full():
@@ -440,15 +423,23 @@ def test_dominant_last_key_in_ragged_tile():
 
 
 @pytest.mark.parametrize("D", [64, 128])
-def test_long_sequence_sampled(D):
-    # 40000 keys: index arithmetic well past 2^16 rows, 625 key tiles
+def test_long_sequence_all_rows(D):
+    # 40000 keys: index arithmetic well past 2^16 rows, 625 key tiles; every
+    # row against the oracle, which runs 2500 query rows at a time
     B, S, H = 1, 40000, 2
     q, k, v = random_qkv(500 + D, B=B, Sq=S, Skv=S, H=H, D=D, gain=math.sqrt(3.0))
     say(f"long sequence S={S} D={D}")
     o, l = cru.attn_fwd_lse(*cuda(q, k, v))
     torch.cuda.synchronize()
-    check_rows(o, l, to_f64(q), to_f64(k), to_f64(v), sample_rows(S, 12, seed=D),
-               TOL_O, TOL_LSE, f"S={S} D={D}")
+    q64, k64, v64 = to_f64(q), to_f64(k), to_f64(v)
+    o64, l64 = to_f64(o), to_f64(l)
+    eo = el = 0.0
+    for a in range(0, S, 2500):
+        o_ref, l_ref = oracle.attention(q64[:, a:a + 2500], k64, v64)
+        eo = max(eo, err(o64[:, a:a + 2500], o_ref))
+        el = max(el, err(l64[:, :, a:a + 2500], l_ref))
+    say(f"  S={S} D={D}: max|dO| = {eo:.3e}, max|dLSE| = {el:.3e} over all {S} rows")
+    assert eo <= TOL_O and el <= TOL_LSE
 
 
 # Batch strides past 2^31 elements: every batch offset needs 64-bit address
