@@ -244,6 +244,39 @@ def ceilings():
     t = timed(lambda: torch.sum(x, dim=0, out=sink))
     out["read_1GiB"] = {"ms_median": t, "GB/s": nb / (t * 1e-3) / 1e9,
                         "frac_of_8000": nb / (t * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    # cold plain copies of several sizes, timed like the merge and layout
+    # legs (a 1 GiB read between reps evicts L2 and the MALL): a straight
+    # line through them splits each copy's time into a fixed cost and a
+    # steady rate, which bounds what a memory-bound launch of a given size
+    # can reach
+    stream = torch.cuda.current_stream()
+    sweep = []
+    for mib in (8, 16, 32, 64, 128, 256, 512):
+        n_el = mib * (1 << 20) // 2
+        src = torch.empty(n_el, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        ts = []
+        for _ in range(25):
+            torch.sum(x, dim=0, out=sink)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dst.copy_(src)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        t = statistics.median(ts)
+        sweep.append({"bytes_rw": 4 * n_el, "ms_median": t, "GB/s": 4 * n_el / (t * 1e-3) / 1e9})
+        del src, dst
+    # least-squares line t = t0 + bytes / rate over the sizes that bracket
+    # the layout and merge launches (64 to 537 MB moved)
+    pts = [(s_["bytes_rw"], s_["ms_median"]) for s_ in sweep[2:6]]
+    mx = statistics.mean(p[0] for p in pts)
+    my = statistics.mean(p[1] for p in pts)
+    slope = sum((p[0] - mx) * (p[1] - my) for p in pts) / sum((p[0] - mx) ** 2 for p in pts)
+    out["cold_copy_sweep"] = {"points": sweep,
+                              "fixed_us": (my - slope * mx) * 1e3,
+                              "steady_GB/s": 1.0 / (slope * 1e-3) / 1e9}
+    del x, y
     for k, v in out.items():
         log(f"[bench] ceiling {k}: {v}")
     print(json.dumps({"ceilings": out}))
