@@ -43,10 +43,25 @@ constexpr int64_t kMaxDim = (int64_t)1 << 30;
 // multiple of this, so none of them can overflow int64_t.
 constexpr int64_t kMaxElems = (int64_t)1 << 48;
 
+// Largest element offset a view may reach (the sum of (size - 1) * stride
+// over its dims).  The kernels form element and byte offsets in int64_t, so
+// bounding the span keeps every offset they form far from overflow.
+constexpr int64_t kMaxSpan = (int64_t)1 << 60;
+
 // a * b for non-negative a, b, saturating at INT64_MAX instead of overflowing
 int64_t mul_sat(int64_t a, int64_t b) {
   if (a == 0 || b == 0) return 0;
   return a > INT64_MAX / b ? INT64_MAX : a * b;
+}
+
+// a + b for non-negative a, b, saturating at INT64_MAX
+int64_t add_sat(int64_t a, int64_t b) { return a > INT64_MAX - b ? INT64_MAX : a + b; }
+
+// largest element offset of a view whose sizes are all >= 1
+int64_t view_span(int n, const int64_t* size, const int64_t* stride) {
+  int64_t span = 0;
+  for (int i = 0; i < n; ++i) span = add_sat(span, mul_sat(size[i] - 1, stride[i]));
+  return span;
 }
 
 int elem_bytes(int dtype) { return dtype == CRU_BF16 ? 2 : 4; }
@@ -73,6 +88,13 @@ cru_status check_tensor(const cru_tensor* t, const char* name) {
   if (t->sb % vec || t->ss % vec || t->sh % vec)
     return fail(CRU_EINVAL, "%s: strides (%lld, %lld, %lld) are not multiples of %lld elements",
                 name, (long long)t->sb, (long long)t->ss, (long long)t->sh, (long long)vec);
+  if (numel > 0) {
+    const int64_t size[4] = {t->B, t->S, t->H, t->D};
+    const int64_t stride[4] = {t->sb, t->ss, t->sh, 1};
+    if (view_span(4, size, stride) >= kMaxSpan)
+      return fail(CRU_EINVAL, "%s: strides (%lld, %lld, %lld) reach past 2^60 elements", name,
+                  (long long)t->sb, (long long)t->ss, (long long)t->sh);
+  }
   return CRU_OK;
 }
 
@@ -100,8 +122,7 @@ bool strides_injective(int n, const int64_t* size, const int64_t* stride) {
   int64_t reach = 0;   // largest offset of the dims taken so far
   for (int i = 0; i < m; ++i) {
     if (st[i] <= reach) return false;
-    reach = reach + mul_sat(sz[i] - 1, st[i]);
-    if (reach < 0) return false;
+    reach = add_sat(reach, mul_sat(sz[i] - 1, st[i]));
   }
   return true;
 }
@@ -137,6 +158,9 @@ cru_status check_lse(const cru_lse* l, const char* name, int64_t B, int64_t H, i
     return fail(CRU_EINVAL, "%s: data is not 4-byte aligned", name);
   const int64_t size[3] = {B, H, S};
   const int64_t stride[3] = {l->sb, l->sh, 1};
+  if (B * H * S > 0 && view_span(3, size, stride) >= kMaxSpan)
+    return fail(CRU_EINVAL, "%s: strides (%lld, %lld, 1) reach past 2^60 elements", name,
+                (long long)l->sb, (long long)l->sh);
   if (!strides_injective(3, size, stride))
     return fail(CRU_EINVAL, "%s: strides (%lld, %lld, 1) make elements overlap", name,
                 (long long)l->sb, (long long)l->sh);

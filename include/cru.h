@@ -48,7 +48,8 @@
  *  - Sizes: each of B, S, H, D at most 2^30 and B*S*H*D at most 2^48
  *    elements; one call's kernel work items (threads, 16-byte vectors) below
  *    2^31 (split larger calls); for the attention, s strides below 2^22
- *    elements.  Larger requests fail with CRU_EINVAL.
+ *    elements; a view's largest element offset (the sum over its dims of
+ *    (size - 1) * stride) below 2^60.  Larger requests fail with CRU_EINVAL.
  *  - All checks run on the host before anything is enqueued.  A failed check
  *    returns a non-zero cru_status, enqueues nothing and leaves a message for
  *    cru_last_error() (thread-local).  The checks follow the three classes of

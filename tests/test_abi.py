@@ -135,6 +135,28 @@ def test_sizes_whose_product_overflows_are_rejected():
     assert "2^48" not in last_error()
 
 
+def test_views_reaching_past_2_60_elements_are_refused():
+    # the sizes are small but a stride is huge: the largest offset the view
+    # reaches would leave no headroom in the kernels' 64-bit offsets
+    far = T(B=2, strides=(1 << 61, 2 * 64, 64))
+    assert fwd(far, T(S=24), T(S=24), T()) == EINVAL
+    assert "2^60" in last_error()
+    assert fwd(T(B=2), T(B=2, S=24), T(B=2, S=24), far) == EINVAL
+    assert "2^60" in last_error()
+    assert h2s([far], 2) == EINVAL
+    assert "2^60" in last_error()
+    # strides whose sum of offsets would pass 2^63 (no wrap-around: refused)
+    wrap = T(B=4, S=2, H=2, strides=((1 << 62) + 64, 1 << 61, 64))
+    assert fwd(T(B=4, S=2), T(B=4, S=24), T(B=4, S=24), wrap) == EINVAL
+    assert "2^60" in last_error()
+    lse = cru.CruLse(FAKE, 2, 2, 16, 1 << 61, 16)
+    assert fwd(T(B=2), T(B=2, S=24), T(B=2, S=24), T(B=2), lse) == EINVAL
+    assert "2^60" in last_error()
+    # just under the limit passes the host checks (stops at the fake pointer)
+    near = T(B=2, strides=((1 << 59), 2 * 64, 64))
+    assert fwd(near, T(B=2, S=24), T(B=2, S=24), T(B=2)) == EDEVICE, last_error()
+
+
 def test_valid_call_reaches_device_check_without_gpu():
     # well-formed arguments pass every host check; the fake pointer is then
     # rejected as not being device memory (or there is no device here)
