@@ -547,7 +547,13 @@ def main():
         "head2seq_o": {"bytes": 2 * tbytes, "ms_median": med2, "ms_min": mn2,
                        "GB/s": 2 * tbytes / (med2 * 1e-3) / 1e9,
                        "frac_hbm_peak": 2 * tbytes / (med2 * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                       "plain_copy_same_bytes_GB/s": 2 * tbytes / (medc2 * 1e-3) / 1e9}}
+                       "plain_copy_same_bytes_GB/s": 2 * tbytes / (medc2 * 1e-3) / 1e9},
+        # both all-to-alls' layouts of a Ulysses step: their bytes over their
+        # summed cold times
+        "seq2head_plus_head2seq": {"bytes": 8 * tbytes, "ms": med1 + med2,
+                                   "GB/s": 8 * tbytes / ((med1 + med2) * 1e-3) / 1e9,
+                                   "frac_hbm_peak": 8 * tbytes / ((med1 + med2) * 1e-3) / 1e9
+                                   / PEAK_HBM_GBS}}
     # Ulysses Anything: the video shape at degree 4 (30 heads -> groups of 8, 8, 7, 7)
     Pa = 4
     ysa = [torch.empty(qv.numel(), dtype=qv.dtype, device=dev) for _ in range(3)]
